@@ -1,0 +1,333 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-attention hot path on one MI355X.
+
+A step is one pass of the path over one batch: kv append of the step's new
+rows, then paged decode (and, for the mixed workload, the causal prefill
+chunks).  Inputs are seeded synthetic batches (workloads.py), resident in HBM
+before timing starts.
+
+Cold-cache timing: the batch is replicated R times in HBM (distinct pools,
+queries and outputs) and consecutive steps rotate over the replicas, so the
+bytes a step reads were last touched R-1 steps earlier -- far more than the
+256 MB Infinity Cache holds.  Each replica's step is captured once in a HIP
+graph; K steps replay those graphs back to back (launch overhead amortised),
+bracketed by synchronisations; ms_per_step is the event time / K.
+
+Roofline of the dominant call (decode): algorithmic bytes per launch (KV rows
+read once -- each physical (block, offset) once -- plus queries and outputs)
+divided by its average duration, timed with HIP events on the launch stream
+while a spin kernel keeps the GPU ahead of the host.
+
+CPU baseline: the CPU oracle (test infrastructure) timed on the host cores on
+the same batch; a bounded sample, reported, never the target.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, datasheet
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, datasheet
+METRIC = ("paged decode KV GB/s and % of HBM peak; seq-steps/s per batch on 1 MI355X")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama_decode", choices=sorted(W.SPECS))
+    ap.add_argument("--replicas", type=int, default=0, help="0 = enough for cold caches")
+    ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--no-graph", action="store_true", help="eager launches")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_kv_cache_407_amd as pkv
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lib = pkv.load_library()
+    log("library", pkv.LIB_PATH, "device", torch.cuda.get_device_name(dev))
+
+    t0 = time.time()
+    b = W.make_batch(args.workload)
+    log(f"generated {args.workload} in {time.time() - t0:.1f}s")
+    spec = b.spec
+    S = b.num_dec
+    C = b.num_pf
+    kvb = W.decode_kv_bytes(b)
+    kv_bytes = kvb["unique"] if spec.shared_prefix else kvb["logical"]
+    q_bytes = b.q_dec.nbytes if S else 0
+    out_bytes = S * spec.num_q_heads * spec.head_dim * 4
+    decode_alg_bytes = kv_bytes + q_bytes + out_bytes
+    append_bytes = 2 * 2 * int((b.slot_mapping >= 0).sum()) * spec.num_kv_heads * spec.head_dim * 2
+    pf_flops = W.prefill_flops(b)
+    max_len = int(b.lens_dec.max()) if S else 1
+    max_q = int(np.diff(b.cu_q_lens).max()) if C else 0
+    part = pkv.decode_partition_size(S, spec.num_q_heads, spec.num_kv_heads, spec.head_dim,
+                                     spec.block_size, max_len, args.partition_size)
+    ws_bytes = pkv.decode_workspace_size(S, spec.num_q_heads, spec.num_kv_heads,
+                                         spec.head_dim, spec.block_size, max_len,
+                                         args.partition_size)
+
+    touched = kv_bytes + append_bytes
+    if C:
+        touched += int(b.lens_pf.astype(np.int64).sum()) * W.kv_token_bytes(b)
+    R = args.replicas or max(1, min(16, math.ceil(2.0e9 / max(touched, 1))))
+    R = max(1, min(R, int(64e9 // b.nbytes_pool())))
+    log(f"replicas {R}: pool {b.nbytes_pool() / 2**30:.2f} GiB each, "
+        f"{touched / 1e6:.1f} MB touched per step; partition {part} tokens")
+
+    def to_dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.float16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.float16)
+        return torch.from_numpy(a).to(dev)
+
+    kc0, vc0 = to_dev(b.k_cache), to_dev(b.v_cache)
+    reps = []
+    for r in range(R):
+        rep = {"kc": kc0 if r == 0 else kc0.clone(), "vc": vc0 if r == 0 else vc0.clone(),
+               "nk": to_dev(b.new_k), "nv": to_dev(b.new_v)}
+        if S:
+            rep["q"] = to_dev(b.q_dec)
+            rep["out"] = torch.empty((S, spec.num_q_heads, spec.head_dim), dtype=torch.float32,
+                                     device=dev)
+            rep["ws"] = (torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+                         if ws_bytes else None)
+        if C:
+            rep["qp"] = to_dev(b.q_pf)
+            rep["outp"] = torch.empty(tuple(b.q_pf.shape), dtype=torch.float32, device=dev)
+        reps.append(rep)
+    slots = to_dev(b.slot_mapping)
+    if S:
+        tab, lens = to_dev(b.tables_dec), to_dev(b.lens_dec)
+    if C:
+        tabp, lensp, cu = to_dev(b.tables_pf), to_dev(b.lens_pf), to_dev(b.cu_q_lens)
+    torch.cuda.synchronize()
+
+    def do_append(rep):
+        pkv.kv_append(rep["nk"], rep["nv"], rep["kc"], rep["vc"], slots)
+
+    def do_decode(rep):
+        pkv.paged_attention_decode(rep["q"], rep["kc"], rep["vc"], tab, lens,
+                                   max_seq_len=max_len, scale=b.scale, out=rep["out"],
+                                   workspace=rep["ws"], partition_size=args.partition_size)
+
+    def do_prefill(rep):
+        pkv.paged_attention_prefill(rep["qp"], cu, rep["kc"], rep["vc"], tabp, lensp,
+                                    max_q_len=max_q, scale=b.scale, out=rep["outp"])
+
+    def step(rep):
+        do_append(rep)
+        if C:
+            do_prefill(rep)
+        if S:
+            do_decode(rep)
+
+    # warmup (eager), then capture one graph per replica
+    for i in range(args.warmup):
+        step(reps[i % R])
+    torch.cuda.synchronize()
+    graphs = None
+    if not args.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for rep in reps:
+                step(rep)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graphs = []
+        for rep in reps:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(rep)
+            graphs.append(g)
+        for g in graphs:   # replays double as extra warmup
+            g.replay()
+        torch.cuda.synchronize()
+
+    # timed region: exactly K steps
+    K = args.steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    e0.record()
+    for i in range(K):
+        if graphs is not None:
+            graphs[i % R].replay()
+        else:
+            step(reps[i % R])
+    e1.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - w0) * 1e3
+    gpu_ms = e0.elapsed_time(e1)
+    ms_per_step = gpu_ms / K
+    log(f"{K} steps: {gpu_ms:.3f} ms GPU, {wall_ms:.3f} ms wall")
+
+    # per-call durations with events (GPU kept ahead of the host by a spin)
+    def timed_calls(fn, n):
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        torch.cuda.synchronize()
+        torch.cuda._sleep(200_000_000)
+        for i in range(n):
+            rep = reps[i % R]
+            starts[i].record()
+            fn(rep)
+            ends[i].record()
+        torch.cuda.synchronize()
+        d = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)]) * 1e3  # us
+        return d
+
+    n_inst = min(K, 200)
+    res = {}
+    if S:
+        d = timed_calls(do_decode, n_inst)
+        res["decode_us"] = d
+    d_app = timed_calls(do_append, n_inst)
+    if C:
+        res["prefill_us"] = timed_calls(do_prefill, n_inst)
+
+    step_s = ms_per_step / 1e3
+    value = kv_bytes / step_s / 1e9 if S else 0.0
+    seqs = S + C
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 in, f32 accumulate",
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload, "description": spec.description,
+            "num_seqs": S, "prefill_chunks": C, "num_q_heads": spec.num_q_heads,
+            "num_kv_heads": spec.num_kv_heads, "head_dim": spec.head_dim,
+            "block_size": spec.block_size, "seq_lens_total": int(b.lens_dec.sum()) if S else 0,
+            "max_seq_len": max_len, "partition_size": part, "replicas": R,
+            "graph": graphs is not None,
+        },
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "seq_steps_per_s": round(seqs / step_s, 1),
+        "kv_bytes_per_step": kv_bytes,
+        "kv_bytes_logical": kvb["logical"],
+        "wall_ms_per_step": round(wall_ms / K, 6),
+        "append_us_mean": round(float(d_app.mean()), 3),
+    }
+    if S:
+        d = res["decode_us"]
+        achieved = decode_alg_bytes / (d.mean() * 1e-6) / 1e9
+        line["roofline"] = {
+            "kernel": "paged_attention_decode (partition kernel + merge kernel when split)",
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "alg_bytes_per_launch": decode_alg_bytes,
+            "us_mean": round(float(d.mean()), 3), "us_p10": round(float(np.percentile(d, 10)), 3),
+            "us_p90": round(float(np.percentile(d, 90)), 3),
+        }
+    if C:
+        d = res["prefill_us"]
+        tf = pf_flops / (d.mean() * 1e-6) / 1e12
+        line["prefill"] = {"flops": pf_flops, "us_mean": round(float(d.mean()), 3),
+                           "tflops": round(tf, 1),
+                           "frac_mfma_f16_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
+                           "tokens_per_s": round(int(b.new_k.shape[0]) / step_s, 1)}
+
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(b, kv_bytes, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(b: W.Batch, kv_bytes: int, budget_s: float) -> dict:
+    """Times the CPU oracle (append + decode [+ prefill]) on a bounded sample
+    of the same batch; the rate is scaled to KV GB/s of the full batch."""
+    import oracle
+    orc = oracle.get()
+    cores = int(os.environ.get("OMP_NUM_THREADS") or len(os.sched_getaffinity(0)))
+    S = b.num_dec
+    Hq = b.spec.num_q_heads
+    # estimate: ~50 M fp64 multiply-adds per second per thread
+    macs = int(b.lens_dec.astype(np.int64).sum()) * Hq * b.spec.head_dim * 2 if S else 0
+    est = macs / (5e7 * cores)
+    frac = 1.0
+    rows = None
+    if est > budget_s:
+        frac = budget_s / est
+        n = max(1, int(S * Hq * frac))
+        rows = np.sort(np.random.default_rng(0).choice(S * Hq, n, replace=False))
+        frac = n / (S * Hq)
+    t0 = time.perf_counter()
+    kc, vc = orc.kv_append(b.new_k, b.new_v, b.k_cache, b.v_cache, b.slot_mapping)
+    t_app = time.perf_counter() - t0
+    reps, t_dec = 0, 0.0
+    while True:
+        t0 = time.perf_counter()
+        if S:
+            orc.decode(b.q_dec, kc, vc, b.tables_dec, b.lens_dec, b.scale, rows=rows)
+        if b.num_pf:
+            orc.prefill(b.q_pf, b.cu_q_lens, kc, vc, b.tables_pf, b.lens_pf, b.scale)
+        t_dec += time.perf_counter() - t0
+        reps += 1
+        if t_dec >= budget_s or reps >= 20 or (frac < 1.0):
+            break
+    step = t_app + (t_dec / reps) / frac
+    sample = (f"{reps} run(s) of oracle decode over {'all' if rows is None else len(rows)} of "
+              f"{S * Hq} (sequence, head) rows, plus one kv append; time scaled to the "
+              f"whole batch")
+    return {"value": round(kv_bytes / step / 1e9, 4), "unit": "GB/s", "cores": cores,
+            "kind": "oracle", "sample": sample, "step_s": round(step, 4),
+            "cpu": _cpu_model()}
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+if __name__ == "__main__":
+    main()

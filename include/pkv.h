@@ -1,0 +1,158 @@
+/*
+ * pkv.h -- paged KV-cache attention for AMD Instinct MI355X (gfx950).
+ *
+ * A C ABI over hand-written HIP kernels.  Every pointer argument named as a
+ * device buffer is a device pointer that the caller allocated and owns; the
+ * library never allocates, frees or synchronises.  Work is enqueued on
+ * `stream` (a hipStream_t; NULL = the default stream), so the return value
+ * reports host-side argument checks and launch status only.
+ *
+ * Layouts (row-major, fp16 = IEEE binary16 bit patterns):
+ *   k_cache, v_cache : [num_blocks][num_kv_heads][block_size][head_dim] fp16
+ *                      A sequence's logically contiguous tokens live in
+ *                      fixed-size physical blocks; logical token t of a
+ *                      sequence sits in block block_tables[seq][t / block_size]
+ *                      at offset t % block_size ("LLM 推理引擎 Continuous
+ *                      Batching 与 PagedAttention：从 vLLM 原理到生产级部署实战",
+ *                      §3.1 and §3.3; "动态批处理算法：连续批处理、In-flight
+ *                      请求管理与 PagedAttention", §4.3).  For one KV head a
+ *                      block is the [block_size][head_dim] tile that the
+ *                      first page's kernel comment describes.
+ *   block_tables     : [num_seqs][max_blocks_per_seq] int32; entries at or
+ *                      beyond ceil(seq_len / block_size) are never read.
+ *   seq_lens         : [num_seqs] int32, tokens held after this step's append.
+ *   Query head h reads KV head h / (num_q_heads / num_kv_heads).
+ *
+ * Supported instances: head_dim 64 or 128, block_size 16 or 32, any
+ * num_q_heads that is a multiple of num_kv_heads.
+ *
+ * Device-side contents cannot be checked without a synchronisation, so the
+ * kernels guard them instead: a slot outside the pool is skipped; a sequence
+ * whose length or block-table entries are out of range gets NaN in every
+ * output element of its rows.  No kernel reads or writes outside the buffers
+ * described by the size arguments.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    PKV_OK = 0,
+    PKV_ERR_INVALID = 1,     /* null pointer, bad size, misaligned buffer */
+    PKV_ERR_UNSUPPORTED = 2, /* no compiled instance for this shape */
+    PKV_ERR_HIP = 3          /* the HIP runtime reported an error */
+};
+
+/* Static description of a status code. */
+const char *pkv_status_string(int status);
+
+/*
+ * kv append: copies each new token's K and V rows into its physical slot
+ * ("LLM 推理引擎 …", §3.2 BlockManager.append_token: a token goes into the
+ * last block while it has room, otherwise into a newly taken block; the
+ * slot = block * block_size + offset names that place).
+ *
+ *   key, value   : [num_tokens][num_kv_heads][head_dim] fp16, device
+ *   k_cache, v_cache : the pools, device, written in place
+ *   slot_mapping : [num_tokens] int32, device; slot < 0 marks a padding row
+ *                  that is skipped; slots must be distinct (two rows with
+ *                  one slot race); a slot >= num_blocks * block_size is
+ *                  skipped.
+ * The fp16 bit patterns are copied unchanged.  num_tokens may be 0.
+ * Buffers must be 16-byte aligned.
+ */
+int pkv_kv_append(const void *key, const void *value, void *k_cache,
+                  void *v_cache, const int32_t *slot_mapping,
+                  int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                  int32_t block_size, int32_t num_blocks, void *stream);
+
+/*
+ * Bytes of device workspace pkv_paged_attention_decode needs for these
+ * arguments (0 when the sequences are not split).  Same meaning of the
+ * arguments as below.
+ */
+size_t pkv_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, int32_t max_seq_len,
+                                 int32_t partition_size);
+
+/*
+ * Tokens per partition the decode uses for these arguments (the library's
+ * choice when partition_size is 0).
+ */
+int32_t pkv_decode_partition_size(int32_t num_seqs, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t block_size, int32_t max_seq_len,
+                                  int32_t partition_size);
+
+/*
+ * Paged attention decode: one query token per sequence attends to all
+ * seq_lens[s] tokens of its sequence through the block table
+ * ("LLM 推理引擎 …", §3.3: block-table indirection, tokens_in_block bound,
+ * running max and sum of exponentials; the V weighting the page leaves out is
+ * out = sum_t softmax(q.k_t * scale)_t v_t).  Softmax and the weighted sum
+ * accumulate in fp32.
+ *
+ *   out          : [num_seqs][num_q_heads][head_dim] float32, device
+ *   q            : [num_seqs][num_q_heads][head_dim] fp16, device
+ *   seq_lens     : each in 1 .. min(max_seq_len, max_blocks_per_seq*block_size)
+ *   max_seq_len  : host-side upper bound of seq_lens (sizes the split)
+ *   scale        : score scale, normally 1/sqrt(head_dim)
+ *   partition_size : tokens per split-sequence partition, a positive
+ *                  multiple of block_size; 0 = library's choice.  Partitions are
+ *                  merged with the log-sum-exp identity of the running max /
+ *                  sum recurrence.
+ *   workspace    : device, at least pkv_decode_workspace_size(...) bytes,
+ *                  16-byte aligned (may be NULL when that size is 0)
+ */
+int pkv_paged_attention_decode(float *out, const void *q, const void *k_cache,
+                               const void *v_cache,
+                               const int32_t *block_tables,
+                               const int32_t *seq_lens, int32_t num_seqs,
+                               int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t block_size,
+                               int32_t num_blocks, int32_t max_blocks_per_seq,
+                               int32_t max_seq_len, float scale,
+                               int32_t partition_size, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+/*
+ * Paged attention prefill of causal chunks whose prefix already sits in
+ * paged blocks ("LLM 推理引擎 …", §4.3 Chunked Prefill and §1.1: the prompt
+ * is processed in chunks; a chunk's query at absolute position p attends to
+ * keys 0..p).  Chunk c owns query rows cu_q_lens[c] .. cu_q_lens[c+1]-1;
+ * its sequence holds seq_lens[c] tokens including the chunk (already
+ * appended with pkv_kv_append), so row j of the chunk sits at position
+ * seq_lens[c] - chunk_len + j.  QK^T and PV run on MFMA (fp16 inputs, fp32
+ * accumulation); the softmax weights enter PV as fp16.
+ *
+ *   out          : [total_q_tokens][num_q_heads][head_dim] float32, device
+ *   q            : [total_q_tokens][num_q_heads][head_dim] fp16, device
+ *   cu_q_lens    : [num_chunks + 1] int32, device, cu_q_lens[0] = 0,
+ *                  non-decreasing, cu_q_lens[num_chunks] = total_q_tokens
+ *   block_tables : [num_chunks][max_blocks_per_seq] int32, device
+ *   seq_lens     : [num_chunks] int32, device, chunk_len <= seq_len
+ *   max_q_len    : host-side upper bound of the chunk lengths
+ */
+int pkv_paged_attention_prefill(float *out, const void *q,
+                                const int32_t *cu_q_lens, const void *k_cache,
+                                const void *v_cache,
+                                const int32_t *block_tables,
+                                const int32_t *seq_lens, int32_t num_chunks,
+                                int32_t total_q_tokens, int32_t max_q_len,
+                                int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size,
+                                int32_t num_blocks, int32_t max_blocks_per_seq,
+                                float scale, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -1,0 +1,186 @@
+"""Paged KV-cache attention for AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over ``libpkv.so`` (hand-written HIP kernels behind the
+C ABI in ``include/pkv.h``).  The functions below only check tensor
+dtypes/devices/shapes and pass raw device pointers plus torch's current HIP
+stream; every step of the computation runs in the library's kernels.  There
+is no fallback: without the built library (``__graft_entry__.build()``)
+importing the functions raises.
+
+Names follow the C ABI without the ``pkv_`` prefix.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from pathlib import Path
+
+import torch
+
+_HERE = Path(__file__).resolve().parent
+LIB_PATH = _HERE / "libpkv.so"
+
+PKV_OK = 0
+
+_lib = None
+
+# (name, restype, argtypes) for every symbol include/pkv.h declares
+_P, _I32, _SZ, _F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+SIGNATURES = {
+    "pkv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "pkv_kv_append": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P]),
+    "pkv_decode_workspace_size": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
+    "pkv_decode_partition_size": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
+    "pkv_paged_attention_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32,
+                                                  _I32, _I32, _I32, _I32, _F, _I32, _P, _SZ, _P]),
+    "pkv_paged_attention_prefill": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32,
+                                                   _I32, _I32, _I32, _I32, _I32, _I32, _F, _P]),
+}
+
+
+class PkvError(RuntimeError):
+    pass
+
+
+def load_library(path: str | Path = LIB_PATH):
+    """Loads libpkv.so and declares its signatures (no GPU needed)."""
+    global _lib
+    if _lib is not None and Path(path) == LIB_PATH:
+        return _lib
+    path = Path(path)
+    if not path.exists():
+        raise PkvError(f"{path} is missing: build it with __graft_entry__.build() "
+                       "(hipcc --offload-arch=gfx950); there is no fallback path")
+    lib = ctypes.CDLL(str(path))
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def _check(rc: int, what: str):
+    if rc != PKV_OK:
+        msg = load_library().pkv_status_string(rc).decode()
+        raise PkvError(f"{what}: {msg} (status {rc})")
+
+
+def _dev(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int | None = None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device, got {t.device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    return t
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _cache_shape(k_cache, v_cache):
+    _dev(k_cache, "k_cache", torch.float16, 4)
+    _dev(v_cache, "v_cache", torch.float16, 4)
+    if k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache shapes differ")
+    return tuple(k_cache.shape)  # NB, Hkv, bs, D
+
+
+def kv_append(key, value, k_cache, v_cache, slot_mapping, stream=None):
+    """Writes key/value [T, Hkv, D] rows into their slots of the caches."""
+    NB, Hkv, bs, D = _cache_shape(k_cache, v_cache)
+    _dev(key, "key", torch.float16, 3)
+    _dev(value, "value", torch.float16, 3)
+    _dev(slot_mapping, "slot_mapping", torch.int32, 1)
+    T = slot_mapping.shape[0]
+    if key.shape != (T, Hkv, D) or value.shape != (T, Hkv, D):
+        raise ValueError(f"key/value must be {(T, Hkv, D)}")
+    rc = load_library().pkv_kv_append(key.data_ptr(), value.data_ptr(), k_cache.data_ptr(),
+                                      v_cache.data_ptr(), slot_mapping.data_ptr(), T, Hkv, D,
+                                      bs, NB, _stream(stream))
+    _check(rc, "kv_append")
+
+
+def decode_partition_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                          max_seq_len, partition_size=0) -> int:
+    return int(load_library().pkv_decode_partition_size(
+        num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_seq_len, partition_size))
+
+
+def decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                          max_seq_len, partition_size=0) -> int:
+    return int(load_library().pkv_decode_workspace_size(
+        num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_seq_len, partition_size))
+
+
+def paged_attention_decode(q, k_cache, v_cache, block_tables, seq_lens, *, max_seq_len: int,
+                           scale: float | None = None, out=None, workspace=None,
+                           partition_size: int = 0, stream=None):
+    """out[S, Hq, D] (float32) of one query token per sequence."""
+    NB, Hkv, bs, D = _cache_shape(k_cache, v_cache)
+    _dev(q, "q", torch.float16, 3)
+    _dev(block_tables, "block_tables", torch.int32, 2)
+    _dev(seq_lens, "seq_lens", torch.int32, 1)
+    S, Hq, Dq = q.shape
+    if Dq != D or block_tables.shape[0] != S or seq_lens.shape[0] != S:
+        raise ValueError("q / block_tables / seq_lens shapes disagree")
+    MB = block_tables.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((S, Hq, D), dtype=torch.float32, device=q.device)
+    _dev(out, "out", torch.float32, 3)
+    if out.shape != (S, Hq, D):
+        raise ValueError("out shape")
+    need = decode_workspace_size(S, Hq, Hkv, D, bs, max_seq_len, partition_size)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr, ws_bytes = 0, 0
+    if workspace is not None:
+        _dev(workspace, "workspace", torch.uint8, 1)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
+    rc = load_library().pkv_paged_attention_decode(
+        out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        block_tables.data_ptr(), seq_lens.data_ptr(), S, Hq, Hkv, D, bs, NB, MB,
+        int(max_seq_len), float(scale), int(partition_size), ws_ptr, ws_bytes, _stream(stream))
+    _check(rc, "paged_attention_decode")
+    return out
+
+
+def paged_attention_prefill(q, cu_q_lens, k_cache, v_cache, block_tables, seq_lens, *,
+                            max_q_len: int, scale: float | None = None, out=None, stream=None):
+    """out[sum C, Hq, D] (float32) of causal chunks on paged prefixes."""
+    NB, Hkv, bs, D = _cache_shape(k_cache, v_cache)
+    _dev(q, "q", torch.float16, 3)
+    _dev(cu_q_lens, "cu_q_lens", torch.int32, 1)
+    _dev(block_tables, "block_tables", torch.int32, 2)
+    _dev(seq_lens, "seq_lens", torch.int32, 1)
+    T, Hq, Dq = q.shape
+    C = seq_lens.shape[0]
+    if Dq != D or cu_q_lens.shape[0] != C + 1 or block_tables.shape[0] != C:
+        raise ValueError("q / cu_q_lens / block_tables / seq_lens shapes disagree")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((T, Hq, D), dtype=torch.float32, device=q.device)
+    _dev(out, "out", torch.float32, 3)
+    if out.shape != (T, Hq, D):
+        raise ValueError("out shape")
+    rc = load_library().pkv_paged_attention_prefill(
+        out.data_ptr(), q.data_ptr(), cu_q_lens.data_ptr(), k_cache.data_ptr(),
+        v_cache.data_ptr(), block_tables.data_ptr(), seq_lens.data_ptr(), C, T,
+        int(max_q_len), Hq, Hkv, D, bs, NB, block_tables.shape[1], float(scale),
+        _stream(stream))
+    _check(rc, "paged_attention_prefill")
+    return out

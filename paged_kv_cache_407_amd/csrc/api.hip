@@ -1,0 +1,215 @@
+// C ABI of libpkv: argument checks, split choice and kernel launches.
+// The functions and their contracts are declared in include/pkv.h.
+#include <math.h>
+#include <stdint.h>
+
+#include "common.hpp"
+#include "kernels.hpp"
+#include "pkv.h"
+
+using namespace pkv;
+
+namespace {
+
+constexpr int kDefaultPartition = 256;  // tokens per split-sequence partition
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool supported(int32_t head_dim, int32_t block_size) {
+  return (head_dim == 64 || head_dim == 128) &&
+         (block_size == 16 || block_size == 32);
+}
+
+int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
+
+// Tokens per partition; 0 when the arguments are invalid.
+int32_t partition_tokens(int32_t block_size, int32_t max_seq_len,
+                         int32_t requested) {
+  if (block_size <= 0 || max_seq_len <= 0) return 0;
+  if (requested > 0) return requested % block_size ? 0 : requested;
+  if (requested < 0) return 0;
+  int64_t part = round_up(kDefaultPartition, block_size);
+  if (max_seq_len <= part) part = round_up(max_seq_len, block_size);
+  return (int32_t)part;
+}
+
+struct WorkspaceLayout {
+  int32_t num_parts = 0;
+  size_t o_off = 0, m_off = 0, l_off = 0, bytes = 0;
+};
+
+WorkspaceLayout layout(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                       int32_t max_seq_len, int32_t part) {
+  WorkspaceLayout w;
+  w.num_parts = (int32_t)((max_seq_len + (int64_t)part - 1) / part);
+  if (w.num_parts <= 1) return w;
+  const size_t rows = (size_t)num_seqs * num_q_heads * w.num_parts;
+  w.o_off = 0;
+  w.m_off = round_up((int64_t)(rows * head_dim * sizeof(float)), 256);
+  w.l_off = w.m_off + round_up((int64_t)(rows * sizeof(float)), 256);
+  w.bytes = w.l_off + round_up((int64_t)(rows * sizeof(float)), 256);
+  return w;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char *pkv_status_string(int status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_INVALID: return "invalid argument";
+    case PKV_ERR_UNSUPPORTED: return "unsupported shape (head_dim 64/128, block_size 16/32)";
+    case PKV_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int pkv_kv_append(const void *key, const void *value, void *k_cache,
+                  void *v_cache, const int32_t *slot_mapping,
+                  int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                  int32_t block_size, int32_t num_blocks, void *stream) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      num_blocks <= 0 || head_dim % 8)
+    return PKV_ERR_INVALID;
+  if (num_tokens == 0) return PKV_OK;
+  if (!key || !value || !k_cache || !v_cache || !slot_mapping)
+    return PKV_ERR_INVALID;
+  if (!aligned16(key) || !aligned16(value) || !aligned16(k_cache) ||
+      !aligned16(v_cache))
+    return PKV_ERR_INVALID;
+  AppendParams p;
+  p.key = (const uint4 *)key;
+  p.value = (const uint4 *)value;
+  p.k_cache = (uint4 *)k_cache;
+  p.v_cache = (uint4 *)v_cache;
+  p.slots = slot_mapping;
+  p.num_tokens = num_tokens;
+  p.num_kv_heads = num_kv_heads;
+  p.chunks_per_row = head_dim / 8;
+  p.block_size = block_size;
+  p.num_slots = (int64_t)num_blocks * block_size;
+  return hip_status(launch_kv_append(p, (hipStream_t)stream));
+}
+
+int32_t pkv_decode_partition_size(int32_t num_seqs, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t block_size, int32_t max_seq_len,
+                                  int32_t partition_size) {
+  (void)num_seqs; (void)num_q_heads; (void)num_kv_heads; (void)head_dim;
+  return partition_tokens(block_size, max_seq_len, partition_size);
+}
+
+size_t pkv_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, int32_t max_seq_len,
+                                 int32_t partition_size) {
+  const int32_t part = pkv_decode_partition_size(
+      num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_seq_len,
+      partition_size);
+  if (part <= 0 || num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
+  return layout(num_seqs, num_q_heads, head_dim, max_seq_len, part).bytes;
+}
+
+int pkv_paged_attention_decode(float *out, const void *q, const void *k_cache,
+                               const void *v_cache,
+                               const int32_t *block_tables,
+                               const int32_t *seq_lens, int32_t num_seqs,
+                               int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t block_size,
+                               int32_t num_blocks, int32_t max_blocks_per_seq,
+                               int32_t max_seq_len, float scale,
+                               int32_t partition_size, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      block_size <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 ||
+      max_seq_len <= 0 || num_q_heads % num_kv_heads || !isfinite(scale))
+    return PKV_ERR_INVALID;
+  if ((int64_t)max_seq_len > (int64_t)max_blocks_per_seq * block_size)
+    return PKV_ERR_INVALID;
+  if (!supported(head_dim, block_size)) return PKV_ERR_UNSUPPORTED;
+  const int32_t part = partition_tokens(block_size, max_seq_len, partition_size);
+  if (part <= 0) return PKV_ERR_INVALID;
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !seq_lens)
+    return PKV_ERR_INVALID;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) ||
+      !aligned16(v_cache))
+    return PKV_ERR_INVALID;
+  const WorkspaceLayout w =
+      layout(num_seqs, num_q_heads, head_dim, max_seq_len, part);
+  if (w.bytes > 0 && (!workspace || workspace_bytes < w.bytes ||
+                      !aligned16(workspace)))
+    return PKV_ERR_INVALID;
+
+  DecodeParams p;
+  p.out = out;
+  p.q = (const _Float16 *)q;
+  p.k_cache = (const _Float16 *)k_cache;
+  p.v_cache = (const _Float16 *)v_cache;
+  p.block_tables = block_tables;
+  p.seq_lens = seq_lens;
+  char *ws = (char *)workspace;
+  p.ws_o = w.bytes ? (float *)(ws + w.o_off) : nullptr;
+  p.ws_m = w.bytes ? (float *)(ws + w.m_off) : nullptr;
+  p.ws_l = w.bytes ? (float *)(ws + w.l_off) : nullptr;
+  p.num_seqs = num_seqs;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.group = num_q_heads / num_kv_heads;
+  p.num_blocks = num_blocks;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.max_seq_len = max_seq_len;
+  p.part_tokens = part;
+  p.num_parts = w.num_parts;
+  p.scale_log2e = scale * kLog2e;
+  return hip_status(launch_decode(p, head_dim, block_size, (hipStream_t)stream));
+}
+
+int pkv_paged_attention_prefill(float *out, const void *q,
+                                const int32_t *cu_q_lens, const void *k_cache,
+                                const void *v_cache,
+                                const int32_t *block_tables,
+                                const int32_t *seq_lens, int32_t num_chunks,
+                                int32_t total_q_tokens, int32_t max_q_len,
+                                int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size,
+                                int32_t num_blocks, int32_t max_blocks_per_seq,
+                                float scale, void *stream) {
+  if (num_chunks < 0 || total_q_tokens < 0 || max_q_len < 0 ||
+      num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      block_size <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 ||
+      num_q_heads % num_kv_heads || !isfinite(scale))
+    return PKV_ERR_INVALID;
+  if (num_q_heads > 65535 || num_chunks > 65535) return PKV_ERR_INVALID;
+  if (!supported(head_dim, block_size)) return PKV_ERR_UNSUPPORTED;
+  if (num_chunks == 0 || total_q_tokens == 0) return PKV_OK;
+  if (!out || !q || !cu_q_lens || !k_cache || !v_cache || !block_tables ||
+      !seq_lens)
+    return PKV_ERR_INVALID;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) ||
+      !aligned16(v_cache))
+    return PKV_ERR_INVALID;
+  PrefillParams p;
+  p.out = out;
+  p.q = (const _Float16 *)q;
+  p.cu_q_lens = cu_q_lens;
+  p.k_cache = (const _Float16 *)k_cache;
+  p.v_cache = (const _Float16 *)v_cache;
+  p.block_tables = block_tables;
+  p.seq_lens = seq_lens;
+  p.num_chunks = num_chunks;
+  p.total_q = total_q_tokens;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.group = num_q_heads / num_kv_heads;
+  p.num_blocks = num_blocks;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.scale_log2e = scale * kLog2e;
+  return hip_status(launch_prefill(p, head_dim, block_size, max_q_len,
+                                   (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,90 @@
+// Device helpers shared by the paged-attention kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kWave = 64;
+
+__host__ __device__ constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// Makes a value the compiler treats as divergent wave-uniform (e.g. the
+// wave index), so that loads addressed by it become scalar loads.
+__device__ __forceinline__ int uniform(int v) {
+  return __builtin_amdgcn_readfirstlane(v);
+}
+
+// DPP move of a float within rows of 16 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                         0xF, 0xF, false));
+}
+
+// Sum over aligned groups of LANES (8 or 16) consecutive lanes; every lane
+// of a group receives the group's sum.  quad_perm swaps pairs, then pairs of
+// pairs; half-row mirror folds quads into 8-lane halves; row mirror folds
+// the two halves of a 16-lane row.
+template <int LANES>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(LANES == 8 || LANES == 16, "group of 8 or 16 lanes");
+  v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp<0x141>(v);  // row_half_mirror
+  if constexpr (LANES == 16) v += dpp<0x140>(v);  // row_mirror
+  return v;
+}
+
+__device__ __forceinline__ float xor_max(float v, int mask) {
+  return fmaxf(v, __shfl_xor(v, mask, kWave));
+}
+__device__ __forceinline__ float xor_sum(float v, int mask) {
+  return v + __shfl_xor(v, mask, kWave);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) {
+  return __builtin_amdgcn_exp2f(x);  // v_exp_f32; exp2(-inf) = 0
+}
+
+__device__ __forceinline__ uint4 ld16(const void *p) {
+  return *reinterpret_cast<const uint4 *>(p);
+}
+__device__ __forceinline__ void st16(void *p, uint4 v) {
+  *reinterpret_cast<uint4 *>(p) = v;
+}
+
+__device__ __forceinline__ h8_t as_h8(uint4 v) {
+  return __builtin_bit_cast(h8_t, v);
+}
+
+// q . k over 8 fp16 pairs, fp32 accumulation (v_dot2c_f32_f16).
+__device__ __forceinline__ float dot8(h8_t a, h8_t b, float acc) {
+  acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(a, a, 0, 1),
+                               __builtin_shufflevector(b, b, 0, 1), acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(a, a, 2, 3),
+                               __builtin_shufflevector(b, b, 2, 3), acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(a, a, 4, 5),
+                               __builtin_shufflevector(b, b, 4, 5), acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(a, a, 6, 7),
+                               __builtin_shufflevector(b, b, 6, 7), acc, false);
+  return acc;
+}
+
+// v_mfma_f32_16x16x32_f16: D(16x16) = A(16x32) B(32x16) + C.  Lane l
+// supplies row l%16 of A and column l%16 of B, each as 8 fp16 values of the
+// contraction index (group l/16); lane l receives D rows 4*(l/16)+r, r<4,
+// of column l%16.
+__device__ __forceinline__ f4_t mfma16x16x32(h8_t a, h8_t b, f4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+}  // namespace pkv

@@ -1,0 +1,55 @@
+// Kernel parameter blocks and launchers (internal to libpkv).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+struct AppendParams {
+  const uint4 *key;      // [T][Hkv][D] fp16, as 16-byte chunks
+  const uint4 *value;
+  uint4 *k_cache;        // [NB][Hkv][BS][D]
+  uint4 *v_cache;
+  const int32_t *slots;  // [T]
+  int32_t num_tokens, num_kv_heads, chunks_per_row, block_size;
+  int64_t num_slots;
+};
+
+struct DecodeParams {
+  float *out;                   // [S][Hq][D]
+  const _Float16 *q;            // [S][Hq][D]
+  const _Float16 *k_cache;      // [NB][Hkv][BS][D]
+  const _Float16 *v_cache;
+  const int32_t *block_tables;  // [S][MB]
+  const int32_t *seq_lens;      // [S]
+  float *ws_o;                  // [S][Hq][NP][D]   (split only)
+  float *ws_m;                  // [S][Hq][NP]
+  float *ws_l;                  // [S][Hq][NP]
+  int32_t num_seqs, num_q_heads, num_kv_heads, group;
+  int32_t num_blocks, max_blocks_per_seq, max_seq_len;
+  int32_t part_tokens, num_parts;
+  float scale_log2e;
+};
+
+struct PrefillParams {
+  float *out;                   // [Tq][Hq][D]
+  const _Float16 *q;            // [Tq][Hq][D]
+  const int32_t *cu_q_lens;     // [C+1]
+  const _Float16 *k_cache;
+  const _Float16 *v_cache;
+  const int32_t *block_tables;  // [C][MB]
+  const int32_t *seq_lens;      // [C]
+  int32_t num_chunks, total_q, num_q_heads, num_kv_heads, group;
+  int32_t num_blocks, max_blocks_per_seq;
+  float scale_log2e;
+};
+
+hipError_t launch_kv_append(const AppendParams &p, hipStream_t stream);
+// D in {64,128}, BS in {16,32}; returns hipErrorInvalidValue otherwise.
+hipError_t launch_decode(const DecodeParams &p, int head_dim, int block_size,
+                         hipStream_t stream);
+hipError_t launch_prefill(const PrefillParams &p, int head_dim,
+                          int block_size, int max_q_len, hipStream_t stream);
+
+}  // namespace pkv
