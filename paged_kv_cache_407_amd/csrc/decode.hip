@@ -77,6 +77,9 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeParams p) {
   const int nblk = cdiv(L, BS);
   const int blk0 = part * part_blocks;
   const int blk1 = min(blk0 + part_blocks, nblk);
+  // Tokens of this partition; a wave step may overhang the partition's last
+  // block, and those zero-filled rows must not enter the softmax.
+  const int tok_end = min(L, blk1 * BS);
   const int32_t *trow = p.block_tables + (size_t)s * p.max_blocks_per_seq;
 
   const int col = lane % LPR;   // 16-byte column within a token row
@@ -123,7 +126,7 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeParams p) {
     for (int i = 0; i < NL; ++i) {
       const int tok = (b + i / LPB) * BS + (i % LPB) * RPL + rrow;
       const float d = group_sum<LPR>(dot8(qv, as_h8(kr[i]), 0.f));
-      sc[i] = tok < L ? d * p.scale_log2e : -INFINITY;
+      sc[i] = tok < tok_end ? d * p.scale_log2e : -INFINITY;
       cmax = fmaxf(cmax, sc[i]);
     }
 #pragma unroll
@@ -136,7 +139,7 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeParams p) {
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       const int tok = (b + i / LPB) * BS + (i % LPB) * RPL + rrow;
-      const bool ok = tok < L;
+      const bool ok = tok < tok_end;
       const float pr = ok ? fast_exp2(sc[i] - mnew) : 0.f;
       const h8_t v = as_h8(ok ? vr[i] : zero);
       lsum += pr;
