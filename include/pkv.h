@@ -105,11 +105,17 @@ int32_t pkv_decode_partition_size(int32_t num_seqs, int32_t num_q_heads,
  *   max_seq_len  : host-side upper bound of seq_lens (sizes the split)
  *   scale        : score scale, normally 1/sqrt(head_dim)
  *   partition_size : tokens per split-sequence partition, a positive
- *                  multiple of block_size; 0 = library's choice.  Partitions are
- *                  merged with the log-sum-exp identity of the running max /
- *                  sum recurrence.
+ *                  multiple of block_size and at most 64 * block_size;
+ *                  0 = library's choice.  Partitions are merged with the
+ *                  log-sum-exp identity of the running max / sum recurrence
+ *                  (a second kernel, enqueued by the same call).
  *   workspace    : device, at least pkv_decode_workspace_size(...) bytes,
- *                  16-byte aligned (may be NULL when that size is 0)
+ *                  16-byte aligned, owned by the caller (may be NULL when
+ *                  that size is 0).  Its contents on entry do not matter and
+ *                  nothing in it survives a call; calls that share a
+ *                  workspace must not run concurrently.
+ * Query heads that share a KV head are served by one workgroup, so each
+ * K/V row is read once for all of them.
  */
 int pkv_paged_attention_decode(float *out, const void *q, const void *k_cache,
                                const void *v_cache,

@@ -127,7 +127,11 @@ def decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_s
 def paged_attention_decode(q, k_cache, v_cache, block_tables, seq_lens, *, max_seq_len: int,
                            scale: float | None = None, out=None, workspace=None,
                            partition_size: int = 0, stream=None):
-    """out[S, Hq, D] (float32) of one query token per sequence."""
+    """out[S, Hq, D] (float32) of one query token per sequence.
+
+    ``workspace`` (uint8, at least ``decode_workspace_size(...)`` bytes) holds
+    the split partials; one buffer serves any number of calls on the same
+    stream.  Without it a buffer is allocated for the call."""
     NB, Hkv, bs, D = _cache_shape(k_cache, v_cache)
     _dev(q, "q", torch.float16, 3)
     _dev(block_tables, "block_tables", torch.int32, 2)

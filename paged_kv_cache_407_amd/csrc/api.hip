@@ -22,17 +22,22 @@ bool supported(int32_t head_dim, int32_t block_size) {
 
 int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 
-// Tokens per partition; 0 when the arguments are invalid.
+// Tokens per partition; 0 when the arguments are invalid.  A partition
+// holds at most kMaxPartBlocks blocks (one VGPR of block ids per wave).
 int32_t partition_tokens(int32_t block_size, int32_t max_seq_len,
                          int32_t requested) {
   if (block_size <= 0 || max_seq_len <= 0) return 0;
-  if (requested > 0) return requested % block_size ? 0 : requested;
+  const int64_t cap = (int64_t)kMaxPartBlocks * block_size;
+  if (requested > 0)
+    return (requested % block_size || requested > cap) ? 0 : requested;
   if (requested < 0) return 0;
   int64_t part = round_up(kDefaultPartition, block_size);
   if (max_seq_len <= part) part = round_up(max_seq_len, block_size);
   return (int32_t)part;
 }
 
+// Split-decode workspace: partial outputs, maxima and sums per (row,
+// partition).  No state survives a call.
 struct WorkspaceLayout {
   int32_t num_parts = 0;
   size_t o_off = 0, m_off = 0, l_off = 0, bytes = 0;
@@ -43,7 +48,8 @@ WorkspaceLayout layout(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
   WorkspaceLayout w;
   w.num_parts = (int32_t)((max_seq_len + (int64_t)part - 1) / part);
   if (w.num_parts <= 1) return w;
-  const size_t rows = (size_t)num_seqs * num_q_heads * w.num_parts;
+  const size_t heads = (size_t)num_seqs * num_q_heads;
+  const size_t rows = heads * w.num_parts;
   w.o_off = 0;
   w.m_off = round_up((int64_t)(rows * head_dim * sizeof(float)), 256);
   w.l_off = w.m_off + round_up((int64_t)(rows * sizeof(float)), 256);

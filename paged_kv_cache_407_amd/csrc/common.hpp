@@ -58,6 +58,14 @@ __device__ __forceinline__ float fast_exp2(float x) {
 __device__ __forceinline__ uint4 ld16(const void *p) {
   return *reinterpret_cast<const uint4 *>(p);
 }
+
+// 16-byte load with the nontemporal hint: data streamed once (the K/V rows
+// of a decode) should not displace reusable lines in the caches.
+typedef unsigned u4v_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld16_nt(const void *p) {
+  const u4v_t v = __builtin_nontemporal_load(reinterpret_cast<const u4v_t *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 __device__ __forceinline__ void st16(void *p, uint4 v) {
   *reinterpret_cast<uint4 *>(p) = v;
 }

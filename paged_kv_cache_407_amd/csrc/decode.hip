@@ -9,24 +9,32 @@
 // normalised exponentials (the page leaves that last step out; this is its
 // plain reading).
 //
-// Design for CDNA4 (wave64): a token row of D fp16 is D/8 lanes x 16 bytes,
-// so one wave-wide 16-byte load reads 64/(D/8) whole rows -- 1 KB of a
-// block's contiguous [block_size][D] tile per instruction, fully coalesced.
-// Each lane keeps 8 query values, takes 8-wide dot products with
-// v_dot2c_f32_f16 and the row sum is finished with DPP inside each row
-// group.  Every lane therefore owns the scores of the very tokens whose V
-// slices it holds, so the PV step needs no data exchange.  Softmax runs in
-// base 2 with scale*log2(e) folded into the scores.  Tokens past seq_len are
-// removed by selecting (never by multiplying: the tail slots may hold NaN).
-//
-// A sequence is cut into partitions of part_tokens; one workgroup of 4 waves
-// takes one (partition, sequence, query head).  Waves take interleaved steps
-// of CH blocks (8 KB of K and 8 KB of V in flight per wave and step), keep a
-// running max / sum / accumulator, and are merged through LDS.  With several
-// partitions the workgroup writes (max, sum, unnormalised output) and
-// decode_merge_kernel combines them: M = max_i m_i, out = sum_i 2^(m_i-M) o_i
-// / sum_i 2^(m_i-M) l_i -- the same rescaling the running recurrence uses,
-// applied across partitions.
+// Design for CDNA4 (wave64):
+// * A token row of D fp16 is D/8 lanes x 16 bytes, so one wave-wide 16-byte
+//   load reads 64/(D/8) whole rows -- 1 KB of a block's contiguous
+//   [block_size][D] tile per instruction.  K/V rows are used once, so they
+//   are loaded with the nontemporal hint.
+// * One workgroup serves GH query heads that share one KV head (grouped
+//   query attention), so a K/V row is read from HBM once for all of them.
+//   Each lane keeps 8 query values per head, takes 8-wide dot products with
+//   v_dot2c_f32_f16 and finishes each row sum with DPP inside its row group;
+//   every lane then owns the scores of exactly the tokens whose V slices it
+//   holds, so the PV step needs no data exchange.
+// * Softmax runs in base 2 with scale*log2(e) folded into the scores.  Tokens
+//   past the partition's end are removed by selecting (never by multiplying:
+//   tail slots may hold NaN).
+// * A sequence is cut into partitions of part_tokens (at most 64 blocks, so
+//   one VGPR holds the partition's block ids: lane j keeps entry j and a
+//   wave reads it with v_readlane).  One workgroup of 4 waves takes one
+//   (partition, sequence, head group); waves take interleaved steps of CH
+//   blocks and are merged through LDS.
+// * With several partitions, each workgroup stores (max, sum, unnormalised
+//   output) and decode_merge_kernel combines them: M = max_i m_i,
+//   out = sum_i 2^(m_i-M) o_i / sum_i 2^(m_i-M) l_i -- the rescaling of the
+//   running recurrence, applied across partitions.  (Merging inside the last
+//   partition to finish would need device-scope release/acquire fences,
+//   which on this chip write back and invalidate the L2 of every XCD per
+//   workgroup; a second launch is far cheaper.)
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -42,145 +50,165 @@ struct DecodeShape {
   static_assert(BS % RPL == 0, "block must hold whole wave loads");
 };
 
-template <int D, int BS>
-__global__ __launch_bounds__(256) void decode_partition_kernel(DecodeParams p) {
+constexpr int kDecodeWaves = 4;
+
+template <int D, int BS, int GH>
+__global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   using Sh = DecodeShape<D, BS>;
   constexpr int LPR = Sh::LPR, RPL = Sh::RPL, LPB = Sh::LPB, CH = Sh::CH,
-                NL = Sh::NL;
-  __shared__ float s_acc[4][D];
-  __shared__ float s_m[4], s_l[4];
-  __shared__ int s_bad[4];
+                NL = Sh::NL, NW = kDecodeWaves;
+  __shared__ float s_acc[NW][GH][D];
+  __shared__ float s_m[NW][GH], s_l[NW][GH];
 
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
+  const int HG = p.num_q_heads / GH;
   int idx = blockIdx.x;
-  const int h = idx % p.num_q_heads;
-  idx /= p.num_q_heads;
+  const int hg = idx % HG;
+  idx /= HG;
   const int s = idx % p.num_seqs;
   const int part = idx / p.num_seqs;
+  const int h0 = hg * GH;
+  const size_t row0 = (size_t)s * p.num_q_heads + h0;  // first output row
 
   const int L = p.seq_lens[s];
-  const size_t row = (size_t)s * p.num_q_heads + h;
-  const bool len_ok =
-      L >= 1 && L <= p.max_seq_len && L <= p.max_blocks_per_seq * BS;
-  if (!len_ok) {
-    // With a split, the merge kernel writes this row.
-    if (p.num_parts == 1 && part == 0)
-      for (int d = threadIdx.x; d < D; d += blockDim.x)
-        p.out[row * D + d] = __builtin_nanf("");
+  if (!(L >= 1 && L <= p.max_seq_len && L <= p.max_blocks_per_seq * BS)) {
+    if (part == 0)
+      for (int i = threadIdx.x; i < GH * D; i += blockDim.x)
+        p.out[row0 * D + i] = __builtin_nanf("");
     return;
   }
-  if (part >= cdiv(L, p.part_tokens)) return;
+  const int np_row = cdiv(L, p.part_tokens);
+  if (part >= np_row) return;
 
-  const int kvh = h / p.group;
+  const int kvh = h0 / p.group;
   const int part_blocks = p.part_tokens / BS;
   const int nblk = cdiv(L, BS);
   const int blk0 = part * part_blocks;
   const int blk1 = min(blk0 + part_blocks, nblk);
-  // Tokens of this partition; a wave step may overhang the partition's last
-  // block, and those zero-filled rows must not enter the softmax.
+  // A wave step may overhang the partition's last block; those zero-filled
+  // rows must not enter the softmax.
   const int tok_end = min(L, blk1 * BS);
+
+  // The partition's block ids, lane j holding entry j; an id outside the
+  // pool poisons the whole sequence (every wave sees the same slice).
   const int32_t *trow = p.block_tables + (size_t)s * p.max_blocks_per_seq;
+  int my_blk = 0;
+  if (lane < blk1 - blk0) my_blk = trow[blk0 + lane];
+  const bool my_bad =
+      lane < blk1 - blk0 && (my_blk < 0 || my_blk >= p.num_blocks);
+  if (my_bad) my_blk = 0;
+  const bool bad = __any(my_bad);
 
   const int col = lane % LPR;   // 16-byte column within a token row
   const int rrow = lane / LPR;  // token row within one wave-wide load
-  const h8_t qv = as_h8(ld16(p.q + row * D + col * 8));
-
-  float m = -INFINITY, lsum = 0.f;
-  float acc[8];
+  h8_t qv[GH];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) acc[k] = 0.f;
-  int bad = 0;
+  for (int g = 0; g < GH; ++g)
+    qv[g] = as_h8(ld16(p.q + (row0 + g) * D + col * 8));
+
+  float m[GH], lsum[GH], acc[GH][8];
+#pragma unroll
+  for (int g = 0; g < GH; ++g) {
+    m[g] = -INFINITY;
+    lsum[g] = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[g][k] = 0.f;
+  }
   const size_t head_elems = (size_t)BS * D;
   const uint4 zero = make_uint4(0, 0, 0, 0);
 
-  for (int b = blk0 + wave * CH; b < blk1; b += 4 * CH) {
+  for (int b = blk0 + wave * CH; b < blk1; b += NW * CH) {
     uint4 kr[NL], vr[NL];
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const int bb = b + c;
-      int phys = 0;
-      if (bb < blk1) {
-        phys = trow[bb];
-        if (phys < 0 || phys >= p.num_blocks) {
-          bad = 1;
-          phys = 0;
-        }
-      }
+      const bool in = bb < blk1;
+      const int phys = __builtin_amdgcn_readlane(my_blk, in ? bb - blk0 : 0);
       const size_t base =
           ((size_t)phys * p.num_kv_heads + kvh) * head_elems + rrow * D + col * 8;
 #pragma unroll
       for (int j = 0; j < LPB; ++j) {
-        if (bb < blk1) {
-          kr[c * LPB + j] = ld16(p.k_cache + base + (size_t)j * RPL * D);
-          vr[c * LPB + j] = ld16(p.v_cache + base + (size_t)j * RPL * D);
+        if (in) {
+          kr[c * LPB + j] = ld16_nt(p.k_cache + base + (size_t)j * RPL * D);
+          vr[c * LPB + j] = ld16_nt(p.v_cache + base + (size_t)j * RPL * D);
         } else {
           kr[c * LPB + j] = zero;
           vr[c * LPB + j] = zero;
         }
       }
     }
-    float sc[NL];
-    float cmax = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const int tok = (b + i / LPB) * BS + (i % LPB) * RPL + rrow;
-      const float d = group_sum<LPR>(dot8(qv, as_h8(kr[i]), 0.f));
-      sc[i] = tok < tok_end ? d * p.scale_log2e : -INFINITY;
-      cmax = fmaxf(cmax, sc[i]);
+    for (int g = 0; g < GH; ++g) {
+      float sc[NL];
+      float cmax = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        const int tok = (b + i / LPB) * BS + (i % LPB) * RPL + rrow;
+        const float d = group_sum<LPR>(dot8(qv[g], as_h8(kr[i]), 0.f));
+        sc[i] = tok < tok_end ? d * p.scale_log2e : -INFINITY;
+        cmax = fmaxf(cmax, sc[i]);
+      }
+#pragma unroll
+      for (int off = LPR; off < kWave; off <<= 1) cmax = xor_max(cmax, off);
+      // the step's first token is always valid, so mnew is finite
+      const float mnew = fmaxf(m[g], cmax);
+      const float alpha = fast_exp2(m[g] - mnew);
+      lsum[g] *= alpha;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[g][k] *= alpha;
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        const int tok = (b + i / LPB) * BS + (i % LPB) * RPL + rrow;
+        const bool ok = tok < tok_end;
+        const float pr = ok ? fast_exp2(sc[i] - mnew) : 0.f;
+        const h8_t v = as_h8(ok ? vr[i] : zero);
+        lsum[g] += pr;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[g][k] = fmaf(pr, (float)v[k], acc[g][k]);
+      }
+      m[g] = mnew;
     }
-#pragma unroll
-    for (int off = LPR; off < kWave; off <<= 1) cmax = xor_max(cmax, off);
-    const float mnew = fmaxf(m, cmax);
-    const float alpha = fast_exp2(m - mnew);
-    lsum *= alpha;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) acc[k] *= alpha;
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const int tok = (b + i / LPB) * BS + (i % LPB) * RPL + rrow;
-      const bool ok = tok < tok_end;
-      const float pr = ok ? fast_exp2(sc[i] - mnew) : 0.f;
-      const h8_t v = as_h8(ok ? vr[i] : zero);
-      lsum += pr;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) acc[k] = fmaf(pr, (float)v[k], acc[k]);
-    }
-    m = mnew;
   }
 
   // Lanes of one row group hold equal sums; add the row groups.
 #pragma unroll
-  for (int off = LPR; off < kWave; off <<= 1) {
-    lsum = xor_sum(lsum, off);
+  for (int g = 0; g < GH; ++g) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) acc[k] = xor_sum(acc[k], off);
-  }
-  if (lane < LPR) {
+    for (int off = LPR; off < kWave; off <<= 1) {
+      lsum[g] = xor_sum(lsum[g], off);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) s_acc[wave][col * 8 + k] = acc[k];
-  }
-  if (lane == 0) {
-    s_m[wave] = m;
-    s_l[wave] = lsum;
-    s_bad[wave] = bad;
+      for (int k = 0; k < 8; ++k) acc[g][k] = xor_sum(acc[g][k], off);
+    }
+    if (lane < LPR) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) s_acc[wave][g][col * 8 + k] = acc[g][k];
+    }
+    if (lane == 0) {
+      s_m[wave][g] = m[g];
+      s_l[wave][g] = lsum[g];
+    }
   }
   __syncthreads();
-  if (threadIdx.x < D) {
-    const int d = threadIdx.x;
-    const float M = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+
+  const bool split = np_row > 1;
+  for (int i = threadIdx.x; i < GH * D; i += blockDim.x) {
+    const int g = i / D, d = i % D;
+    float M = s_m[0][g];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, s_m[w][g]);
     float o = 0.f, l = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float e = fast_exp2(s_m[w] - M);  // an idle wave has m = -inf
-      o = fmaf(e, s_acc[w][d], o);
-      l = fmaf(e, s_l[w], l);
+    for (int w = 0; w < NW; ++w) {
+      const float e = fast_exp2(s_m[w][g] - M);  // an idle wave has m = -inf
+      o = fmaf(e, s_acc[w][g][d], o);
+      l = fmaf(e, s_l[w][g], l);
     }
-    if (s_bad[0] | s_bad[1] | s_bad[2] | s_bad[3]) o = __builtin_nanf("");
-    if (p.num_parts == 1) {
-      p.out[row * D + d] = o / l;
+    if (bad) o = __builtin_nanf("");
+    if (!split) {
+      p.out[(row0 + g) * D + d] = o / l;
     } else {
-      const size_t pi = row * p.num_parts + part;
+      const size_t pi = (row0 + g) * p.num_parts + part;
       p.ws_o[pi * D + d] = o;
       if (d == 0) {
         p.ws_m[pi] = M;
@@ -196,44 +224,57 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeParams p) {
   const int s = (int)(row / p.num_q_heads);
   const int d = threadIdx.x;
   const int L = p.seq_lens[s];
-  const bool len_ok =
-      L >= 1 && L <= p.max_seq_len && L <= p.max_blocks_per_seq * BS;
-  if (!len_ok) {
-    p.out[row * D + d] = __builtin_nanf("");
-    return;
-  }
+  if (!(L >= 1 && L <= p.max_seq_len && L <= p.max_blocks_per_seq * BS))
+    return;  // the partition kernel wrote NaN
   const int np = cdiv(L, p.part_tokens);
+  if (np == 1) return;  // written directly by the partition kernel
   const size_t base = row * p.num_parts;
   float M = -INFINITY;
-  for (int i = 0; i < np; ++i) M = fmaxf(M, p.ws_m[base + i]);
+  for (int j = 0; j < np; ++j) M = fmaxf(M, p.ws_m[base + j]);
   float o = 0.f, l = 0.f;
-  for (int i = 0; i < np; ++i) {
-    const float e = fast_exp2(p.ws_m[base + i] - M);
-    o = fmaf(e, p.ws_o[(base + i) * D + d], o);
-    l = fmaf(e, p.ws_l[base + i], l);
+  for (int j = 0; j < np; ++j) {
+    const float e = fast_exp2(p.ws_m[base + j] - M);
+    o = fmaf(e, p.ws_o[(base + j) * D + d], o);
+    l = fmaf(e, p.ws_l[base + j], l);
   }
   p.out[row * D + d] = o / l;
 }
 
-template <int D, int BS>
+template <int D, int BS, int GH>
 static hipError_t launch(const DecodeParams &p, hipStream_t stream) {
-  const int64_t rows = (int64_t)p.num_seqs * p.num_q_heads;
-  const int64_t grid = rows * p.num_parts;
+  const int64_t grid =
+      (int64_t)p.num_parts * p.num_seqs * (p.num_q_heads / GH);
   if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  decode_partition_kernel<D, BS><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(p);
+  decode_kernel<D, BS, GH>
+      <<<dim3((unsigned)grid), dim3(64 * kDecodeWaves), 0, stream>>>(p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.num_parts == 1) return e;
+  const int64_t rows = (int64_t)p.num_seqs * p.num_q_heads;
   decode_merge_kernel<D, BS><<<dim3((unsigned)rows), dim3(D), 0, stream>>>(p);
   return hipGetLastError();
 }
 
+// Heads per workgroup: the largest of 8, 4, 2, 1 that divides the group of
+// query heads sharing one KV head.
+template <int D, int BS>
+static hipError_t launch_heads(const DecodeParams &p, hipStream_t stream) {
+  if (p.group % 8 == 0) return launch<D, BS, 8>(p, stream);
+  if (p.group % 4 == 0) return launch<D, BS, 4>(p, stream);
+  if (p.group % 2 == 0) return launch<D, BS, 2>(p, stream);
+  return launch<D, BS, 1>(p, stream);
+}
+
 hipError_t launch_decode(const DecodeParams &p, int head_dim, int block_size,
                          hipStream_t stream) {
-  if (head_dim == 128 && block_size == 16) return launch<128, 16>(p, stream);
-  if (head_dim == 128 && block_size == 32) return launch<128, 32>(p, stream);
-  if (head_dim == 64 && block_size == 16) return launch<64, 16>(p, stream);
-  if (head_dim == 64 && block_size == 32) return launch<64, 32>(p, stream);
+  if (p.part_tokens <= 0 || p.part_tokens % block_size ||
+      p.part_tokens > kMaxPartBlocks * block_size || p.group <= 0 ||
+      p.num_q_heads % p.group)
+    return hipErrorInvalidValue;
+  if (head_dim == 128 && block_size == 16) return launch_heads<128, 16>(p, stream);
+  if (head_dim == 128 && block_size == 32) return launch_heads<128, 32>(p, stream);
+  if (head_dim == 64 && block_size == 16) return launch_heads<64, 16>(p, stream);
+  if (head_dim == 64 && block_size == 32) return launch_heads<64, 32>(p, stream);
   return hipErrorInvalidValue;
 }
 

@@ -47,6 +47,8 @@ struct PrefillParams {
 
 hipError_t launch_kv_append(const AppendParams &p, hipStream_t stream);
 // D in {64,128}, BS in {16,32}; returns hipErrorInvalidValue otherwise.
+// part_tokens must be a multiple of BS and at most kMaxPartBlocks * BS.
+constexpr int kMaxPartBlocks = 64;
 hipError_t launch_decode(const DecodeParams &p, int head_dim, int block_size,
                          hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams &p, int head_dim,

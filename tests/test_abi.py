@@ -64,6 +64,11 @@ def test_partition_and_workspace_policy():
     # a requested size must be a multiple of the block size
     assert pkv.decode_partition_size(8, 32, 32, 128, 16, 1000, 24) == 0
     assert pkv.decode_partition_size(8, 32, 32, 128, 16, 1000, 32) == 32
+    # at most 64 blocks per partition
+    assert pkv.decode_partition_size(8, 32, 32, 128, 16, 4096, 1024) == 1024
+    assert pkv.decode_partition_size(8, 32, 32, 128, 16, 4096, 1040) == 0
+    assert pkv.decode_partition_size(8, 32, 32, 128, 32, 4096, 2048) == 2048
+
 
 
 def test_invalid_arguments_are_rejected_on_the_host():
