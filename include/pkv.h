@@ -103,7 +103,7 @@ int32_t pkv_decode_partition_size(int32_t num_seqs, int32_t num_q_heads,
  *   q            : [num_seqs][num_q_heads][head_dim] fp16, device
  *   seq_lens     : each in 1 .. min(max_seq_len, max_blocks_per_seq*block_size)
  *   max_seq_len  : host-side upper bound of seq_lens (sizes the split)
- *   scale        : score scale, normally 1/sqrt(head_dim)
+ *   scale        : score scale, finite and > 0, normally 1/sqrt(head_dim)
  *   partition_size : tokens per split-sequence partition, a positive
  *                  multiple of block_size and at most 64 * block_size;
  *                  0 = library's choice.  Partitions are merged with the
@@ -144,7 +144,9 @@ int pkv_paged_attention_decode(float *out, const void *q, const void *k_cache,
  *                  non-decreasing, cu_q_lens[num_chunks] = total_q_tokens
  *   block_tables : [num_chunks][max_blocks_per_seq] int32, device
  *   seq_lens     : [num_chunks] int32, device, chunk_len <= seq_len
- *   max_q_len    : host-side upper bound of the chunk lengths
+ *   max_q_len    : host-side upper bound of the chunk lengths (rows past
+ *                  it are not computed)
+ *   scale        : as for the decode
  */
 int pkv_paged_attention_prefill(float *out, const void *q,
                                 const int32_t *cu_q_lens, const void *k_cache,

@@ -131,7 +131,7 @@ int pkv_paged_attention_decode(float *out, const void *q, const void *k_cache,
                                size_t workspace_bytes, void *stream) {
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
       block_size <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 ||
-      max_seq_len <= 0 || num_q_heads % num_kv_heads || !isfinite(scale))
+      max_seq_len <= 0 || num_q_heads % num_kv_heads || !isfinite(scale) || !(scale > 0.f))
     return PKV_ERR_INVALID;
   if ((int64_t)max_seq_len > (int64_t)max_blocks_per_seq * block_size)
     return PKV_ERR_INVALID;
@@ -187,7 +187,7 @@ int pkv_paged_attention_prefill(float *out, const void *q,
   if (num_chunks < 0 || total_q_tokens < 0 || max_q_len < 0 ||
       num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
       block_size <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 ||
-      num_q_heads % num_kv_heads || !isfinite(scale))
+      num_q_heads % num_kv_heads || !isfinite(scale) || !(scale > 0.f))
     return PKV_ERR_INVALID;
   if (num_q_heads > 65535 || num_chunks > 65535) return PKV_ERR_INVALID;
   if (!supported(head_dim, block_size)) return PKV_ERR_UNSUPPORTED;

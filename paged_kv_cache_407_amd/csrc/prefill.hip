@@ -7,46 +7,64 @@
 // P + j of its sequence and attends to keys 0 .. P + j, read through the
 // block table exactly as the decode does.
 //
-// Design for CDNA4: one workgroup of 4 waves takes a 64-row query tile of one
-// (chunk, head); each wave owns 16 query rows.  Key/value tiles of 64 tokens
-// are gathered block by block (one block-table lookup per block) from HBM
-// into LDS with 16-byte loads.  Per tile and wave:
-//   S^T = K Q^T    (v_mfma_f32_16x16x32_f16; A = 16 keys x 32 dims from LDS,
-//                   B = the wave's 16 query rows, kept in registers)
-//   online softmax (base 2, running max and sum per query row; the row's
-//                   values sit in the 4 lanes l%16 = row, so the max and sum
-//                   need two cross-lane steps)
-//   O^T += V^T P^T (the accumulator layout of S^T is exactly the B-operand
-//                   layout of P^T, so the fp16 weights never leave their
-//                   lanes; V^T is read from the row-major V tile in LDS).
-// Computing the transposed products keeps each query row's statistics and
-// its output columns in the same lanes, so the rescale by 2^(m_old - m_new)
-// needs no exchange.  Keys above the diagonal are removed by selection;
-// tiles wholly above it are never loaded.
+// Design for CDNA4 (gfx950, wave64, v_mfma_f32_16x16x32_f16):
+// * One workgroup of 4 waves takes a 128-row query tile of one (chunk, head);
+//   each wave owns 32 query rows (two 16-column MFMA blocks), so every
+//   operand fragment read from LDS feeds two MFMAs.
+// * Key/value tiles of 64 tokens are gathered from the paged pool (one
+//   block-table lookup per thread and tile) into double-buffered LDS: the
+//   next tile's global loads are in flight while the current one is
+//   consumed.  K is stored row-major; V is stored transposed ([dim][key]).
+// * Per tile and wave:
+//     S^T = K Q^T     A = 16 keys x 32 dims from LDS, B = the wave's query
+//                     rows, kept in registers;
+//     online softmax  base 2, running max and sum per query row; a row's
+//                     values sit in the 4 lanes with the same l % 16, so the
+//                     max needs two cross-lane steps; the running max only
+//                     moves when a row's maximum exceeds it by 2^8 (the
+//                     weights, at most 256, stay exact enough in fp16), so
+//                     the O rescale is rare;
+//     O^T += V^T P^T  the accumulator layout of S^T is the B-operand layout
+//                     of P^T, so the fp16 weights never leave their lanes.
+//   The 16 keys of each S^T block are taken in a permuted order chosen so
+//   that lane group g ends up holding 8 consecutive keys of each 32-key
+//   step; the V^T operand of PV is then one 16-byte LDS read.
+// * Keys above the diagonal are removed by selection in the diagonal tiles
+//   only; a wave skips tiles that lie wholly above its rows.  The heaviest
+//   query tiles (last in their chunk) are dispatched first.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace pkv {
 
+// log2 of the largest softmax weight tolerated before the running maximum is
+// moved (weights enter the PV product as fp16)
+constexpr float kLazyRescale = 8.f;
+
 template <int D, int BS>
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
-  constexpr int BM = 64, BN = 64;
-  constexpr int KS = D / 32;        // MFMA steps over the head dimension
-  constexpr int DT = D / 16;        // 16-wide output column tiles
-  constexpr int CPR = D / 8;        // 16-byte chunks per token row
-  constexpr int STR = D + 8;        // LDS row stride in fp16 (16-byte pad)
-  constexpr int NCH = BN * CPR / 256;
-  constexpr int NBT = BN / BS;      // blocks per key tile
-  static_assert(NCH * 256 == BN * CPR, "tile load split");
-  __shared__ __attribute__((aligned(16))) _Float16 sK[BN * STR];
-  __shared__ __attribute__((aligned(16))) _Float16 sV[BN * STR];
-  __shared__ int sPhys[NBT];
+__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p,
+                                                         int num_qtiles) {
+  constexpr int BM = 128, BN = 64, WROWS = 32;
+  constexpr int KS = D / 32;    // MFMA steps over the head dimension (QK)
+  constexpr int DT = D / 16;    // 16-row blocks of O^T (PV)
+  constexpr int KPT = D / 32;   // keys per thread in a tile load
+  constexpr int NKG = BN / KPT; // key groups of a tile load
+  constexpr int KSTR = D + 8;   // K tile row stride in fp16 (16-byte pad)
+  constexpr int VSTR = BN + 8;  // V^T tile row stride in fp16
+  static_assert(NKG * (D / 8) == 256, "one 16-byte chunk per thread and key");
+  static_assert(BS % KPT == 0, "a thread's keys share a block");
+  __shared__ __attribute__((aligned(16))) _Float16 sK[2][BN * KSTR];
+  __shared__ __attribute__((aligned(16))) _Float16 sV[2][D * VSTR];
   __shared__ int sBad;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = uniform(tid >> 6);
-  const int qt = blockIdx.x, h = blockIdx.y, c = blockIdx.z;
+  int idx = blockIdx.x;
+  const int h = idx % p.num_q_heads;
+  idx /= p.num_q_heads;
+  const int c = idx % p.num_chunks;
+  const int qt = num_qtiles - 1 - idx / p.num_chunks;
   const int q_begin = p.cu_q_lens[c], q_end = p.cu_q_lens[c + 1];
   if (q_begin < 0 || q_end > p.total_q || q_end < q_begin) return;
   const int qlen = q_end - q_begin;
@@ -65,137 +83,212 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
     return;
   }
 
-  const int g = lane >> 4;          // contraction group of this lane
-  const int lc = lane & 15;         // row / column index of this lane
-  const int qr = row0 + wave * 16 + lc;   // query row (within the chunk)
-  const int qpos = P + qr;                // its position in the sequence
+  const int g = lane >> 4;   // contraction group of this lane
+  const int lc = lane & 15;  // row / column index of this lane
+  const int wq0 = row0 + wave * WROWS;  // first query row of this wave
   const int kvh = h / p.group;
   const int kv_end = P + min(row0 + BM, qlen);
   const int ntiles = cdiv(kv_end, BN);
   const int32_t *trow = p.block_tables + (size_t)c * p.max_blocks_per_seq;
 
-  h8_t qf[KS];
+  // The wave's query rows as B operands: column lc of block qb, dims
+  // 32kk + 8g .. +7.
+  h8_t qf[KS][2];
 #pragma unroll
-  for (int kk = 0; kk < KS; ++kk) {
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (qr < qlen)
-      v = ld16(p.q + ((size_t)(q_begin + qr) * Hq + h) * D + 32 * kk + 8 * g);
-    qf[kk] = as_h8(v);
+  for (int qb = 0; qb < 2; ++qb) {
+    const int qr = wq0 + 16 * qb + lc;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (qr < qlen)
+        v = ld16(p.q + ((size_t)(q_begin + qr) * Hq + h) * D + 32 * kk + 8 * g);
+      qf[kk][qb] = as_h8(v);
+    }
   }
 
-  f4_t o[DT];
+  // Tile loader: thread owns keys KPT*lkg .. +KPT-1 and dims 8*lcc .. +7.
+  // The block id of a later tile is fetched one tile ahead and only checked
+  // where it is used: a branch on it right after its load would wait for
+  // every load issued before it (memory counters retire in order), which
+  // would stall the K/V prefetch.
+  constexpr int kNoBlock = -2147483647 - 1;
+  const int lkg = tid % NKG, lcc = tid / NKG;
+  auto lookup = [&](int t) -> int {
+    const int pos = t * BN + KPT * lkg;
+    if (t >= ntiles || pos >= L) return kNoBlock;
+    return trow[pos / BS];
+  };
+  // Loads are unconditional (an absent key reads block 0, in bounds) and
+  // absent keys are zeroed when the tile is stored: a load under a branch
+  // would make the compiler wait for it inside the branch, serialising the
+  // tile's loads.
+  uint4 kreg[KPT], vreg[KPT];
+  unsigned live = 0;  // bit i: key i of this thread's slice exists
+  auto load = [&](int t, int ph) {
+    if (ph != kNoBlock && (ph < 0 || ph >= p.num_blocks)) {
+      sBad = 1;
+      ph = kNoBlock;
+    }
+    live = 0;
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) o[dt] = f4_t{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, l = 0.f;
-  if (tid == 0) sBad = 0;
+    for (int i = 0; i < KPT; ++i) {
+      const int pos = t * BN + KPT * lkg + i;
+      const bool ok = ph != kNoBlock && pos < L;
+      live |= (unsigned)ok << i;
+      const size_t off =
+          ok ? (((size_t)ph * p.num_kv_heads + kvh) * BS + pos % BS) * D + 8 * lcc
+             : (size_t)8 * lcc;
+      kreg[i] = ld16(p.k_cache + off);
+      vreg[i] = ld16(p.v_cache + off);
+    }
+  };
+  auto store = [&](int buf) {
+    const uint4 zero = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      if (!((live >> i) & 1)) kreg[i] = vreg[i] = zero;
+      st16(&sK[buf][(KPT * lkg + i) * KSTR + 8 * lcc], kreg[i]);
+    }
+    // V^T: dim 8*lcc + j, keys KPT*lkg .. +KPT-1 (KPT*2 contiguous bytes)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      _Float16 *dst = &sV[buf][(8 * lcc + j) * VSTR + KPT * lkg];
+      if constexpr (KPT == 4) {
+        h4_t t;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) t[i] = as_h8(vreg[i])[j];
+        *reinterpret_cast<h4_t *>(dst) = t;
+      } else {
+        h2_t t;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) t[i] = as_h8(vreg[i])[j];
+        *reinterpret_cast<h2_t *>(dst) = t;
+      }
+    }
+  };
 
+  f4_t o[DT][2];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+    o[dt][0] = o[dt][1] = f4_t{0.f, 0.f, 0.f, 0.f};
+  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+
+  if (tid == 0) sBad = 0;
+  __syncthreads();
+  int ph_next = lookup(0);
+  load(0, ph_next);
+  ph_next = lookup(1);
+  store(0);
+  __syncthreads();
+
+  // The wave computes nothing when all its rows lie past the chunk.
+  const bool wave_live = wq0 < qlen;
   for (int kt = 0; kt < ntiles; ++kt) {
+    const int buf = kt & 1;
     const int kbase = kt * BN;
-    __syncthreads();  // the previous tile is consumed
-    if (tid < NBT) {
-      const int pos = kbase + tid * BS;
-      int ph = -1;
-      if (pos < L) {
-        ph = trow[pos / BS];
-        if (ph < 0 || ph >= p.num_blocks) {
-          sBad = 1;
-          ph = -1;
+    if (kt + 1 < ntiles) {
+      load(kt + 1, ph_next);
+      ph_next = lookup(kt + 2);
+    }
+    // skip a tile that lies wholly above this wave's diagonal
+    if (wave_live && kbase <= P + wq0 + WROWS - 1) {
+      const _Float16 *Kt = sK[buf];
+      const _Float16 *Vt = sV[buf];
+      f4_t st[4][2];
+#pragma unroll
+      for (int mm = 0; mm < 4; ++mm) {
+        // A row lc of block mm is key 32*(mm/2) + 8*(lc/4) + 4*(mm%2) + lc%4
+        const int krow = 32 * (mm >> 1) + 8 * (lc >> 2) + 4 * (mm & 1) + (lc & 3);
+        st[mm][0] = st[mm][1] = f4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+          const h8_t a = as_h8(ld16(&Kt[krow * KSTR + 32 * kk + 8 * g]));
+          st[mm][0] = mfma16x16x32(a, qf[kk][0], st[mm][0]);
+          st[mm][1] = mfma16x16x32(a, qf[kk][1], st[mm][1]);
         }
       }
-      sPhys[tid] = ph;
-    }
-    __syncthreads();
+      // lane holds keys kbase + 32*(mm/2) + 8g + 4*(mm%2) + r of column lc
+      const bool diag = kbase + BN - 1 > P + wq0;
+      h8_t pb[2][2];
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int id = tid + 256 * i;
-      const int t = id / CPR, cc = id % CPR;
-      const int pos = kbase + t;
-      const int ph = sPhys[t / BS];
-      uint4 kv = make_uint4(0, 0, 0, 0), vv = kv;
-      if (pos < L && ph >= 0) {
-        const size_t off =
-            (((size_t)ph * p.num_kv_heads + kvh) * BS + pos % BS) * D + cc * 8;
-        kv = ld16(p.k_cache + off);
-        vv = ld16(p.v_cache + off);
+      for (int qb = 0; qb < 2; ++qb) {
+        // raw scores; the scale (> 0) is applied inside the exponent
+        if (diag) {
+          const int qpos = P + wq0 + 16 * qb + lc;
+#pragma unroll
+          for (int mm = 0; mm < 4; ++mm)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int kpos = kbase + 32 * (mm >> 1) + 8 * g + 4 * (mm & 1) + r;
+              if (kpos > qpos) st[mm][qb][r] = -INFINITY;
+            }
+        }
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int mm = 0; mm < 4; ++mm)
+          tmax = fmaxf(tmax, fmaxf(fmaxf(st[mm][qb][0], st[mm][qb][1]),
+                                   fmaxf(st[mm][qb][2], st[mm][qb][3])));
+        tmax = xor_max(tmax, 16);
+        tmax = xor_max(tmax, 32);
+        // Lazy rescaling: the running maximum m only moves when some row's
+        // maximum exceeds it by more than 2^8, so weights stay below 256
+        // (exact enough in fp16) and the O rescale is rare.  Key 0 is
+        // visible to every row in the first tile, so m is finite from then
+        // on and exp2(-inf) = 0 removes masked keys.
+        const float tm = tmax * p.scale_log2e;
+        if (__any(tm > m[qb] + kLazyRescale)) {
+          const float mnew = fmaxf(m[qb], tm);
+          const float alpha = fast_exp2(m[qb] - mnew);
+          m[qb] = mnew;
+          l[qb] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) o[dt][qb] *= alpha;
+        }
+        const float nm = -m[qb];
+        float psum = 0.f;
+#pragma unroll
+        for (int mm = 0; mm < 4; ++mm) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float e = fast_exp2(fmaf(st[mm][qb][r], p.scale_log2e, nm));
+            psum += e;
+            pb[mm >> 1][qb][4 * (mm & 1) + r] = (_Float16)e;
+          }
+        }
+        l[qb] += psum;
       }
-      st16(&sK[t * STR + cc * 8], kv);
-      st16(&sV[t * STR + cc * 8], vv);
+      // O^T[d][q] += sum_k V^T[d][k] P^T[k][q]; slot j of lane group g is key
+      // 32ks + 8g + j on both sides.
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const h8_t a = as_h8(ld16(&Vt[(16 * dt + lc) * VSTR + 32 * ks + 8 * g]));
+          o[dt][0] = mfma16x16x32(a, pb[ks][0], o[dt][0]);
+          o[dt][1] = mfma16x16x32(a, pb[ks][1], o[dt][1]);
+        }
+      }
     }
+    if (kt + 1 < ntiles) store(buf ^ 1);
     __syncthreads();
+  }
 
-    // S^T for 4 sub-tiles of 16 keys: lane holds keys kbase+16mm+4g+r of
-    // query row lc.
-    f4_t st[4];
+  const bool bad = sBad != 0;
 #pragma unroll
-    for (int mm = 0; mm < 4; ++mm) {
-      st[mm] = f4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk) {
-        const h8_t a = as_h8(ld16(&sK[(16 * mm + lc) * STR + 32 * kk + 8 * g]));
-        st[mm] = mfma16x16x32(a, qf[kk], st[mm]);
-      }
-    }
-    float sv[16];
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int mm = 0; mm < 4; ++mm) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int kpos = kbase + 16 * mm + 4 * g + r;
-        const float x = st[mm][r] * p.scale_log2e;
-        sv[mm * 4 + r] = kpos <= qpos ? x : -INFINITY;
-        tmax = fmaxf(tmax, sv[mm * 4 + r]);
-      }
-    }
-    tmax = xor_max(tmax, 16);
-    tmax = xor_max(tmax, 32);
-    const float mnew = fmaxf(m, tmax);   // key 0 is always visible: finite
-    const float alpha = fast_exp2(m - mnew);
-    m = mnew;
-    h8_t pb[2];
-    float psum = 0.f;
-#pragma unroll
-    for (int mm = 0; mm < 4; ++mm) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int kpos = kbase + 16 * mm + 4 * g + r;
-        const float pr = kpos <= qpos ? fast_exp2(sv[mm * 4 + r] - mnew) : 0.f;
-        const _Float16 ph = (_Float16)pr;
-        psum += (float)ph;
-        pb[mm >> 1][(mm & 1) * 4 + r] = ph;
-      }
-    }
-    l = l * alpha + psum;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
-    // O^T[d][row] += sum_k V[k][d] P[row][k]; contraction slot 8g+r is key
-    // 32ks+4g+r, slot 8g+4+r is key 32ks+16+4g+r (matching pb's layout).
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+  for (int qb = 0; qb < 2; ++qb) {
+    float lt = xor_sum(l[qb], 16);
+    lt = xor_sum(lt, 32);
+    const int qr = wq0 + 16 * qb + lc;
+    if (qr < qlen) {
+      float *orow = p.out + ((size_t)(q_begin + qr) * Hq + h) * D;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        h8_t a;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          a[r] = sV[(32 * ks + 4 * g + r) * STR + 16 * dt + lc];
-          a[4 + r] = sV[(32 * ks + 16 + 4 * g + r) * STR + 16 * dt + lc];
-        }
-        o[dt] = mfma16x16x32(a, pb[ks], o[dt]);
+        f4_t r = o[dt][qb] / lt;
+        if (bad)
+          r = f4_t{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
+                   __builtin_nanf("")};
+        *reinterpret_cast<f4_t *>(orow + 16 * dt + 4 * g) = r;
       }
-    }
-  }
-
-  l = xor_sum(l, 16);
-  l = xor_sum(l, 32);
-  if (qr < qlen) {
-    float *orow = p.out + ((size_t)(q_begin + qr) * Hq + h) * D;
-    const bool bad = sBad != 0;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      f4_t r = o[dt] / l;
-      if (bad) r = f4_t{__builtin_nanf(""), __builtin_nanf(""),
-                        __builtin_nanf(""), __builtin_nanf("")};
-      *reinterpret_cast<f4_t *>(orow + 16 * dt + 4 * g) = r;
     }
   }
 }
@@ -204,8 +297,10 @@ template <int D, int BS>
 static hipError_t launch(const PrefillParams &p, int max_q_len,
                          hipStream_t stream) {
   if (p.num_chunks == 0 || max_q_len == 0) return hipSuccess;
-  const dim3 grid(cdiv(max_q_len, 64), p.num_q_heads, p.num_chunks);
-  prefill_kernel<D, BS><<<grid, dim3(256), 0, stream>>>(p);
+  const int qtiles = cdiv(max_q_len, 128);
+  const int64_t grid = (int64_t)qtiles * p.num_chunks * p.num_q_heads;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  prefill_kernel<D, BS><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(p, qtiles);
   return hipGetLastError();
 }
 

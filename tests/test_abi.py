@@ -92,11 +92,14 @@ def test_invalid_arguments_are_rejected_on_the_host():
     assert dec(P, P, P, P, P, P, 2, 4, 4, 128, 16, 8, 4, 65, 0.1, 0, None, 0, None) == 1
     # split needed but no workspace
     assert dec(P, P, P, P, P, P, 2, 4, 4, 128, 16, 8, 64, 1024, 0.1, 0, None, 0, None) == 1
-    # non-finite scale
+    # non-finite or non-positive scale
     assert dec(P, P, P, P, P, P, 2, 4, 4, 128, 16, 8, 4, 64, float("nan"), 0, None, 0, None) == 1
+    assert dec(P, P, P, P, P, P, 2, 4, 4, 128, 16, 8, 4, 64, 0.0, 0, None, 0, None) == 1
+    assert dec(P, P, P, P, P, P, 2, 4, 4, 128, 16, 8, 4, 64, -0.1, 0, None, 0, None) == 1
     pre = lib.pkv_paged_attention_prefill
     assert pre(P, P, P, P, P, P, P, 1, 8, 8, 4, 3, 128, 16, 8, 4, 0.1, None) == 1
     assert pre(P, P, P, P, P, P, P, 1, 8, 8, 4, 4, 80, 16, 8, 4, 0.1, None) == 2
+    assert pre(P, P, P, P, P, P, P, 1, 8, 8, 4, 4, 128, 16, 8, 4, -1.0, None) == 1
     assert pre(None, None, None, None, None, None, None, 0, 0, 0, 4, 4, 128, 16, 8, 4, 0.1, None) == 0
 
 
