@@ -60,11 +60,130 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="eager launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run three plain 1 GiB device copies (the known-size "
+                         "kernel that scales the HBM byte counters)")
+    ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH",
+                                                          "COPY_WRITE"),
+                    help="turn four rocprofv3 --pmc output folders (FETCH_SIZE and "
+                         "WRITE_SIZE of this workload's decode, then of the copy "
+                         "calibration) into the traffic summary under profiles/")
     return ap.parse_args()
+
+
+# --------------------------------------------------------------- HBM traffic
+PROFILES = os.path.join(ROOT, "profiles")
+DECODE_SOURCES = ["paged_kv_cache_407_amd/csrc/decode.hip",
+                  "paged_kv_cache_407_amd/csrc/common.hpp",
+                  "paged_kv_cache_407_amd/csrc/kernels.hpp"]
+COPY_BYTES = 1 << 30
+
+
+def decode_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_path(workload: str) -> str:
+    return os.path.join(PROFILES, f"decode_{workload}_hbm_traffic.txt")
+
+
+def copy_calibration():
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"three copies of {COPY_BYTES} bytes done")
+
+
+def _pmc_means(folder: str, counter: str) -> dict:
+    """Mean counter value (KiB per dispatch) per kernel name."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {folder}")
+    vals = {}
+    for row in csv.DictReader(open(files[0])):
+        if row["Counter_Name"] == counter:
+            vals.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in vals.items()}
+
+
+def summarize_pmc(workload: str, fetch_dir, write_dir, cfetch_dir, cwrite_dir):
+    """HBM bytes per decode call = FETCH_SIZE and WRITE_SIZE of its kernels,
+    each scaled by (known bytes / counter reading) of a plain 1 GiB copy."""
+    fetch = _pmc_means(fetch_dir, "FETCH_SIZE")
+    write = _pmc_means(write_dir, "WRITE_SIZE")
+    cf = _pmc_means(cfetch_dir, "FETCH_SIZE")
+    cw = _pmc_means(cwrite_dir, "WRITE_SIZE")
+    copy_k = [k for k in cf if "copy" in k.lower() or "elementwise" in k.lower()]
+    if not copy_k:
+        raise SystemExit(f"no copy kernel among {list(cf)}")
+    ck = max(copy_k, key=lambda k: cf[k])
+    f_fetch = COPY_BYTES / (cf[ck] * 1024)
+    f_write = COPY_BYTES / (cw[ck] * 1024)
+    dec = [k for k in fetch if "decode" in k]
+    lines = [f"# HBM traffic of one paged_attention_decode call, workload {workload}",
+             f"decode_source_sha256_16: {decode_source_hash()}",
+             f"copy_kernel: {ck}",
+             f"copy_bytes_read: {COPY_BYTES}",
+             f"copy_FETCH_SIZE_KiB: {cf[ck]:.1f}",
+             f"copy_WRITE_SIZE_KiB: {cw[ck]:.1f}",
+             f"fetch_scale: {f_fetch:.4f}",
+             f"write_scale: {f_write:.4f}"]
+    tot_r = tot_w = 0.0
+    for k in sorted(dec):
+        r = fetch[k] * 1024 * f_fetch
+        w = write.get(k, 0.0) * 1024 * f_write
+        tot_r += r
+        tot_w += w
+        lines.append(f"kernel: {k} | FETCH_SIZE_KiB {fetch[k]:.1f} | WRITE_SIZE_KiB "
+                     f"{write.get(k, 0.0):.1f} | read_bytes {r:.0f} | written_bytes {w:.0f}")
+    lines.append(f"traffic_bytes_per_call: {tot_r + tot_w:.0f}")
+    lines.append("commands (from the repository root, TMPDIR=/tmp):")
+    lines.append(f"  rocprofv3 --pmc FETCH_SIZE -f csv --kernel-include-regex pkv -d <dir> -- "
+                 f"python3 bench.py --workload {workload} --steps 10 --warmup 2 "
+                 f"--no-cpu-baseline --no-graph")
+    lines.append("  (the same with WRITE_SIZE)")
+    lines.append("  rocprofv3 --pmc FETCH_SIZE -f csv -d <dir> -- python3 bench.py "
+                 "--copy-calibration   (and WRITE_SIZE)")
+    lines.append(f"  python3 bench.py --workload {workload} --summarize-pmc "
+                 "<fetch dir> <write dir> <copy fetch dir> <copy write dir>")
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(traffic_path(workload), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def measured_traffic(workload: str):
+    """Traffic per decode call from the committed summary, or None when there
+    is none or the decode kernel has changed since it was measured."""
+    try:
+        kv = {}
+        for line in open(traffic_path(workload)):
+            if ": " in line and not line.startswith(("#", " ")):
+                k, v = line.split(": ", 1)
+                kv[k] = v.strip()
+        if kv.get("decode_source_sha256_16") != decode_source_hash():
+            return None
+        return int(float(kv["traffic_bytes_per_call"]))
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        summarize_pmc(args.workload, *args.summarize_pmc)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -79,6 +198,9 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     lib = pkv.load_library()
     log("library", pkv.LIB_PATH, "device", torch.cuda.get_device_name(dev))
 
@@ -260,7 +382,8 @@ def main():
         line["roofline"] = {
             "kernel": "paged_attention_decode (partition kernel + merge kernel when split)",
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(args.workload),
             "alg_bytes_per_launch": decode_alg_bytes,
             "us_mean": round(float(d.mean()), 3), "us_p10": round(float(np.percentile(d, 10)), 3),
             "us_p90": round(float(np.percentile(d, 90)), 3),
