@@ -1,6 +1,8 @@
 // C ABI of libpkv: argument checks, split choice and kernel launches.
 // The functions and their contracts are declared in include/pkv.h.
 #include <math.h>
+
+#include <algorithm>
 #include <stdint.h>
 
 #include "common.hpp"
@@ -11,7 +13,12 @@ using namespace pkv;
 
 namespace {
 
-constexpr int kDefaultPartition = 256;  // tokens per split-sequence partition
+// Default split: the largest partition (1024, 512 or 256 tokens, at most 64
+// blocks) that still gives at least kTargetWorkgroups decode workgroups, so
+// long sequences run few, long workgroups and short batches still fill the
+// chip's 256 CUs several times over.
+constexpr int kTargetWorkgroups = 4096;
+constexpr int kPartitionChoices[] = {1024, 512, 256};
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -24,14 +31,22 @@ int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 
 // Tokens per partition; 0 when the arguments are invalid.  A partition
 // holds at most kMaxPartBlocks blocks (one VGPR of block ids per wave).
-int32_t partition_tokens(int32_t block_size, int32_t max_seq_len,
-                         int32_t requested) {
+int32_t partition_tokens(int32_t num_seqs, int32_t num_q_heads,
+                         int32_t num_kv_heads, int32_t block_size,
+                         int32_t max_seq_len, int32_t requested) {
   if (block_size <= 0 || max_seq_len <= 0) return 0;
   const int64_t cap = (int64_t)kMaxPartBlocks * block_size;
   if (requested > 0)
     return (requested % block_size || requested > cap) ? 0 : requested;
   if (requested < 0) return 0;
-  int64_t part = round_up(kDefaultPartition, block_size);
+  int64_t rows = (int64_t)(num_seqs > 0 ? num_seqs : 1) * (num_q_heads > 0 ? num_q_heads : 1);
+  if (num_q_heads > 0 && num_kv_heads > 0 && num_q_heads % num_kv_heads == 0)
+    rows /= heads_per_workgroup(num_q_heads / num_kv_heads);
+  int64_t part = 0;
+  for (int choice : kPartitionChoices) {
+    part = std::min<int64_t>(round_up(choice, block_size), cap);
+    if (rows * ((max_seq_len + part - 1) / part) >= kTargetWorkgroups) break;
+  }
   if (max_seq_len <= part) part = round_up(max_seq_len, block_size);
   return (int32_t)part;
 }
@@ -104,8 +119,9 @@ int32_t pkv_decode_partition_size(int32_t num_seqs, int32_t num_q_heads,
                                   int32_t num_kv_heads, int32_t head_dim,
                                   int32_t block_size, int32_t max_seq_len,
                                   int32_t partition_size) {
-  (void)num_seqs; (void)num_q_heads; (void)num_kv_heads; (void)head_dim;
-  return partition_tokens(block_size, max_seq_len, partition_size);
+  (void)head_dim;
+  return partition_tokens(num_seqs, num_q_heads, num_kv_heads, block_size,
+                          max_seq_len, partition_size);
 }
 
 size_t pkv_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
@@ -136,7 +152,8 @@ int pkv_paged_attention_decode(float *out, const void *q, const void *k_cache,
   if ((int64_t)max_seq_len > (int64_t)max_blocks_per_seq * block_size)
     return PKV_ERR_INVALID;
   if (!supported(head_dim, block_size)) return PKV_ERR_UNSUPPORTED;
-  const int32_t part = partition_tokens(block_size, max_seq_len, partition_size);
+  const int32_t part = partition_tokens(num_seqs, num_q_heads, num_kv_heads,
+                                        block_size, max_seq_len, partition_size);
   if (part <= 0) return PKV_ERR_INVALID;
   if (num_seqs == 0) return PKV_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !seq_lens)

@@ -49,6 +49,11 @@ hipError_t launch_kv_append(const AppendParams &p, hipStream_t stream);
 // D in {64,128}, BS in {16,32}; returns hipErrorInvalidValue otherwise.
 // part_tokens must be a multiple of BS and at most kMaxPartBlocks * BS.
 constexpr int kMaxPartBlocks = 64;
+// Query heads one decode workgroup serves: the largest of 8, 4, 2, 1 that
+// divides the group of query heads sharing one KV head.
+inline int heads_per_workgroup(int group) {
+  return group % 8 == 0 ? 8 : group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1;
+}
 hipError_t launch_decode(const DecodeParams &p, int head_dim, int block_size,
                          hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams &p, int head_dim,

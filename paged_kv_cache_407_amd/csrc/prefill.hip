@@ -41,6 +41,15 @@ namespace pkv {
 // moved (weights enter the PV product as fp16)
 constexpr float kLazyRescale = 8.f;
 
+// LDS layout, chosen for this chip's LDS (128 banks of 4 bytes; a 16-byte
+// access is served 32 lanes at a time): the K tile's 16-byte slot of row r is
+// XORed with 2*bit5(r), and lane group g of a QK^T operand supplies the head
+// dimensions of slot KS*g + kk at step kk (any slot-to-k assignment is valid
+// as long as the K and Q operands agree).  With a 17-slot row stride the
+// operand reads and the tile stores are then free of bank conflicts; V^T rows
+// take a 10-slot stride, which makes the PV operand reads conflict-free.
+__device__ __forceinline__ int ksw(int r) { return (r >> 4) & 2; }
+
 template <int D, int BS>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p,
                                                          int num_qtiles) {
@@ -50,7 +59,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p,
   constexpr int KPT = D / 32;   // keys per thread in a tile load
   constexpr int NKG = BN / KPT; // key groups of a tile load
   constexpr int KSTR = D + 8;   // K tile row stride in fp16 (16-byte pad)
-  constexpr int VSTR = BN + 8;  // V^T tile row stride in fp16
+  constexpr int VSTR = BN + 16; // V^T tile row stride in fp16 (10 slots)
   static_assert(NKG * (D / 8) == 256, "one 16-byte chunk per thread and key");
   static_assert(BS % KPT == 0, "a thread's keys share a block");
   __shared__ __attribute__((aligned(16))) _Float16 sK[2][BN * KSTR];
@@ -91,8 +100,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p,
   const int ntiles = cdiv(kv_end, BN);
   const int32_t *trow = p.block_tables + (size_t)c * p.max_blocks_per_seq;
 
-  // The wave's query rows as B operands: column lc of block qb, dims
-  // 32kk + 8g .. +7.
+  // The wave's query rows as B operands: column lc of block qb, dims of
+  // slot KS*g + kk (8 per slot).
   h8_t qf[KS][2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
@@ -101,7 +110,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p,
     for (int kk = 0; kk < KS; ++kk) {
       uint4 v = make_uint4(0, 0, 0, 0);
       if (qr < qlen)
-        v = ld16(p.q + ((size_t)(q_begin + qr) * Hq + h) * D + 32 * kk + 8 * g);
+        v = ld16(p.q + ((size_t)(q_begin + qr) * Hq + h) * D + 8 * (KS * g + kk));
       qf[kk][qb] = as_h8(v);
     }
   }
@@ -147,7 +156,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p,
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       if (!((live >> i) & 1)) kreg[i] = vreg[i] = zero;
-      st16(&sK[buf][(KPT * lkg + i) * KSTR + 8 * lcc], kreg[i]);
+      const int row = KPT * lkg + i;
+      st16(&sK[buf][row * KSTR + 8 * (lcc ^ ksw(row))], kreg[i]);
     }
     // V^T: dim 8*lcc + j, keys KPT*lkg .. +KPT-1 (KPT*2 contiguous bytes)
 #pragma unroll
@@ -194,17 +204,33 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p,
     if (wave_live && kbase <= P + wq0 + WROWS - 1) {
       const _Float16 *Kt = sK[buf];
       const _Float16 *Vt = sV[buf];
+      // S^T: the head-dimension step is the outer loop, so the eight
+      // accumulators (4 key blocks x 2 query blocks) are independent and
+      // back-to-back MFMAs never wait on each other; each step's four K
+      // fragments are read one step ahead.
       f4_t st[4][2];
+      h8_t fa[2][4];
+      int krow[4], ksl[4];
 #pragma unroll
       for (int mm = 0; mm < 4; ++mm) {
         // A row lc of block mm is key 32*(mm/2) + 8*(lc/4) + 4*(mm%2) + lc%4
-        const int krow = 32 * (mm >> 1) + 8 * (lc >> 2) + 4 * (mm & 1) + (lc & 3);
+        krow[mm] = 32 * (mm >> 1) + 8 * (lc >> 2) + 4 * (mm & 1) + (lc & 3);
+        ksl[mm] = ksw(krow[mm]);
         st[mm][0] = st[mm][1] = f4_t{0.f, 0.f, 0.f, 0.f};
+      }
+      auto read_k = [&](int kk, h8_t *dst) {
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-          const h8_t a = as_h8(ld16(&Kt[krow * KSTR + 32 * kk + 8 * g]));
-          st[mm][0] = mfma16x16x32(a, qf[kk][0], st[mm][0]);
-          st[mm][1] = mfma16x16x32(a, qf[kk][1], st[mm][1]);
+        for (int mm = 0; mm < 4; ++mm)
+          dst[mm] = as_h8(ld16(&Kt[krow[mm] * KSTR + 8 * ((KS * g + kk) ^ ksl[mm])]));
+      };
+      read_k(0, fa[0]);
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        if (kk + 1 < KS) read_k(kk + 1, fa[(kk + 1) & 1]);
+#pragma unroll
+        for (int mm = 0; mm < 4; ++mm) {
+          st[mm][0] = mfma16x16x32(fa[kk & 1][mm], qf[kk][0], st[mm][0]);
+          st[mm][1] = mfma16x16x32(fa[kk & 1][mm], qf[kk][1], st[mm][1]);
         }
       }
       // lane holds keys kbase + 32*(mm/2) + 8g + 4*(mm%2) + r of column lc
@@ -259,11 +285,19 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p,
       }
       // O^T[d][q] += sum_k V^T[d][k] P^T[k][q]; slot j of lane group g is key
       // 32ks + 8g + j on both sides.
+      // V^T fragments of the first PV step are read together; each one's
+      // slot is refilled with the second step's fragment once consumed.
+      h8_t fb[DT];
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        fb[dt] = as_h8(ld16(&Vt[(16 * dt + lc) * VSTR + 8 * g]));
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          const h8_t a = as_h8(ld16(&Vt[(16 * dt + lc) * VSTR + 32 * ks + 8 * g]));
+          const h8_t a = fb[dt];
+          if (ks == 0)  // fetch the second step's fragment in its place
+            fb[dt] = as_h8(ld16(&Vt[(16 * dt + lc) * VSTR + 32 + 8 * g]));
           o[dt][0] = mfma16x16x32(a, pb[ks][0], o[dt][0]);
           o[dt][1] = mfma16x16x32(a, pb[ks][1], o[dt][1]);
         }
@@ -281,9 +315,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p,
     const int qr = wq0 + 16 * qb + lc;
     if (qr < qlen) {
       float *orow = p.out + ((size_t)(q_begin + qr) * Hq + h) * D;
+      const float inv = 1.f / lt;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        f4_t r = o[dt][qb] / lt;
+        f4_t r = o[dt][qb] * inv;
         if (bad)
           r = f4_t{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
                    __builtin_nanf("")};

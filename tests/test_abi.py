@@ -56,10 +56,14 @@ def test_partition_and_workspace_policy():
     # short sequences are not split and need no workspace
     assert pkv.decode_partition_size(32, 32, 32, 128, 16, 200) == 208
     assert pkv.decode_workspace_size(32, 32, 32, 128, 16, 200) == 0
-    # long ones are split into 256-token partitions
-    assert pkv.decode_partition_size(8, 32, 32, 128, 16, 32768) == 256
+    # long ones are split: the largest of 1024 / 512 / 256 tokens that still
+    # gives at least 4096 workgroups
+    assert pkv.decode_partition_size(8, 32, 32, 128, 16, 32768) == 1024      # 8 x 32K
+    assert pkv.decode_partition_size(60, 32, 32, 128, 16, 2031) == 512       # mixed step
+    assert pkv.decode_partition_size(32, 32, 32, 128, 16, 1017) == 256       # batch 32
+    assert pkv.decode_partition_size(256, 64, 8, 128, 32, 4096) == 1024      # GQA 64/8
     ws = pkv.decode_workspace_size(8, 32, 32, 128, 16, 32768)
-    rows = 8 * 32 * 128
+    rows = 8 * 32 * 32
     assert ws >= rows * (128 + 2) * 4
     # a requested size must be a multiple of the block size
     assert pkv.decode_partition_size(8, 32, 32, 128, 16, 1000, 24) == 0
