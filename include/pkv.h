@@ -46,7 +46,8 @@ enum {
     PKV_OK = 0,
     PKV_ERR_INVALID = 1,     /* null pointer, bad size, misaligned buffer */
     PKV_ERR_UNSUPPORTED = 2, /* no compiled instance for this shape */
-    PKV_ERR_HIP = 3          /* the HIP runtime reported an error */
+    PKV_ERR_HIP = 3,         /* the HIP runtime reported an error */
+    PKV_ERR_NO_BLOCKS = 4    /* block manager: not enough free blocks */
 };
 
 /* Static description of a status code. */
@@ -158,6 +159,61 @@ int pkv_paged_attention_prefill(float *out, const void *q,
                                 int32_t head_dim, int32_t block_size,
                                 int32_t num_blocks, int32_t max_blocks_per_seq,
                                 float scale, void *stream);
+
+/*
+ * Host-side block manager (plain host code, no device calls, not
+ * thread-safe): the free list and per-request block tables that produce the
+ * block_tables / seq_lens / slot_mapping arguments above ("LLM 推理引擎 …",
+ * §3.2 BlockManager: the free list starts as block ids 0 .. N-1 and blocks
+ * are taken from its end; a request of n tokens takes ceil(n / block_size)
+ * blocks or, when too few are free, none; a new token goes into the last
+ * block while it has room, otherwise into a newly taken block; freed blocks
+ * are appended to the free list.  §4.1: a shared prefix is whole blocks
+ * referenced by several tables, returned to the free list when the last
+ * reference goes).  Request ids are caller-chosen 64-bit integers.
+ */
+typedef struct pkv_block_manager pkv_block_manager;
+
+/* NULL when the arguments are invalid or memory runs out. */
+pkv_block_manager *pkv_bm_create(int32_t num_blocks, int32_t block_size);
+void pkv_bm_destroy(pkv_block_manager *bm);
+/* Free blocks, or -1 for a NULL manager. */
+int32_t pkv_bm_num_free(const pkv_block_manager *bm);
+/* A new request holding num_tokens tokens (e.g. a prompt to prefill).
+ * PKV_ERR_INVALID if the id exists; PKV_ERR_NO_BLOCKS (nothing taken) if
+ * fewer than ceil(num_tokens / block_size) blocks are free. */
+int pkv_bm_allocate(pkv_block_manager *bm, int64_t request_id, int32_t num_tokens);
+/* Adds one token to a request; *slot = block * block_size + offset of the
+ * new token.  PKV_ERR_NO_BLOCKS (no change) if a block is needed and none
+ * is free. */
+int pkv_bm_append_token(pkv_block_manager *bm, int64_t request_id, int32_t *slot);
+/* One token for each of count distinct requests (a decode step's
+ * slot_mapping); all or nothing. */
+int pkv_bm_append_tokens(pkv_block_manager *bm, const int64_t *request_ids,
+                         int32_t count, int32_t *slots);
+/* A new request whose table starts with the parent's blocks that lie wholly
+ * inside its first prefix_tokens tokens (shared, reference-counted); it
+ * holds those blocks' tokens. */
+int pkv_bm_fork(pkv_block_manager *bm, int64_t parent_id, int64_t child_id,
+                int32_t prefix_tokens);
+/* Drops a request; blocks no other table references return to the free list. */
+int pkv_bm_free(pkv_block_manager *bm, int64_t request_id);
+/* Tokens held by a request, or -1 if unknown. */
+int32_t pkv_bm_seq_len(const pkv_block_manager *bm, int64_t request_id);
+/* Copies up to capacity block ids of a request (host memory); returns the
+ * table's length, or -1 if unknown. */
+int32_t pkv_bm_block_table(const pkv_block_manager *bm, int64_t request_id,
+                           int32_t *blocks, int32_t capacity);
+/* Host arrays for the kernels: block_tables [count][max_blocks_per_seq]
+ * (unused entries = pad_block) and seq_lens [count]. */
+int pkv_bm_build_tables(const pkv_block_manager *bm, const int64_t *request_ids,
+                        int32_t count, int32_t max_blocks_per_seq,
+                        int32_t pad_block, int32_t *block_tables,
+                        int32_t *seq_lens);
+/* Slots of positions first_pos .. first_pos+count-1 of a request (which
+ * must already hold them), e.g. the slot_mapping of a prompt's prefill. */
+int pkv_bm_slots(const pkv_block_manager *bm, int64_t request_id,
+                 int32_t first_pos, int32_t count, int32_t *slots);
 
 #ifdef __cplusplus
 }

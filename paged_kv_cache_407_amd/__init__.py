@@ -26,6 +26,7 @@ _lib = None
 
 # (name, restype, argtypes) for every symbol include/pkv.h declares
 _P, _I32, _SZ, _F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+_I64 = ctypes.c_int64
 SIGNATURES = {
     "pkv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "pkv_kv_append": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P]),
@@ -35,7 +36,20 @@ SIGNATURES = {
                                                   _I32, _I32, _I32, _I32, _F, _I32, _P, _SZ, _P]),
     "pkv_paged_attention_prefill": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32,
                                                    _I32, _I32, _I32, _I32, _I32, _I32, _F, _P]),
+    "pkv_bm_create": (_P, [_I32, _I32]),
+    "pkv_bm_destroy": (None, [_P]),
+    "pkv_bm_num_free": (_I32, [_P]),
+    "pkv_bm_allocate": (ctypes.c_int, [_P, _I64, _I32]),
+    "pkv_bm_append_token": (ctypes.c_int, [_P, _I64, _P]),
+    "pkv_bm_append_tokens": (ctypes.c_int, [_P, _P, _I32, _P]),
+    "pkv_bm_fork": (ctypes.c_int, [_P, _I64, _I64, _I32]),
+    "pkv_bm_free": (ctypes.c_int, [_P, _I64]),
+    "pkv_bm_seq_len": (_I32, [_P, _I64]),
+    "pkv_bm_block_table": (_I32, [_P, _I64, _P, _I32]),
+    "pkv_bm_build_tables": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _P, _P]),
+    "pkv_bm_slots": (ctypes.c_int, [_P, _I64, _I32, _I32, _P]),
 }
+PKV_ERR_NO_BLOCKS = 4
 
 
 class PkvError(RuntimeError):
@@ -188,3 +202,97 @@ def paged_attention_prefill(q, cu_q_lens, k_cache, v_cache, block_tables, seq_le
         _stream(stream))
     _check(rc, "paged_attention_prefill")
     return out
+
+
+class OutOfBlocks(PkvError):
+    """The block manager has too few free blocks (nothing was changed)."""
+
+
+class BlockManager:
+    """Host free-list block manager of libpkv (``pkv_bm_*``): allocates
+    ceil(n / block_size) blocks per request from a LIFO free list, appends
+    tokens, shares whole prefix blocks with reference counts, and builds the
+    block tables and slot mappings the kernels take (as numpy int32 arrays)."""
+
+    def __init__(self, num_blocks: int, block_size: int):
+        import numpy as np
+        self._np = np
+        self._lib = load_library()
+        self._h = self._lib.pkv_bm_create(int(num_blocks), int(block_size))
+        if not self._h:
+            raise PkvError("pkv_bm_create: invalid arguments")
+        self.num_blocks, self.block_size = int(num_blocks), int(block_size)
+
+    def close(self):
+        if self._h:
+            self._lib.pkv_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def _rc(self, rc, what):
+        if rc == PKV_ERR_NO_BLOCKS:
+            raise OutOfBlocks(f"{what}: not enough free KV blocks")
+        _check(rc, what)
+
+    @property
+    def num_free(self) -> int:
+        return int(self._lib.pkv_bm_num_free(self._h))
+
+    def allocate(self, request_id: int, num_tokens: int):
+        self._rc(self._lib.pkv_bm_allocate(self._h, int(request_id), int(num_tokens)), "allocate")
+
+    def append_token(self, request_id: int) -> int:
+        slot = ctypes.c_int32()
+        self._rc(self._lib.pkv_bm_append_token(self._h, int(request_id), ctypes.byref(slot)),
+                 "append_token")
+        return slot.value
+
+    def append_tokens(self, request_ids):
+        np = self._np
+        ids = np.ascontiguousarray(request_ids, dtype=np.int64)
+        slots = np.empty(ids.shape[0], np.int32)
+        self._rc(self._lib.pkv_bm_append_tokens(self._h, ids.ctypes.data, ids.shape[0],
+                                                slots.ctypes.data), "append_tokens")
+        return slots
+
+    def fork(self, parent_id: int, child_id: int, prefix_tokens: int):
+        self._rc(self._lib.pkv_bm_fork(self._h, int(parent_id), int(child_id),
+                                       int(prefix_tokens)), "fork")
+
+    def free(self, request_id: int):
+        self._rc(self._lib.pkv_bm_free(self._h, int(request_id)), "free")
+
+    def seq_len(self, request_id: int) -> int:
+        return int(self._lib.pkv_bm_seq_len(self._h, int(request_id)))
+
+    def block_table(self, request_id: int):
+        np = self._np
+        n = self._lib.pkv_bm_block_table(self._h, int(request_id), None, 0)
+        if n < 0:
+            raise PkvError("block_table: unknown request")
+        out = np.empty(n, np.int32)
+        self._lib.pkv_bm_block_table(self._h, int(request_id), out.ctypes.data, n)
+        return out
+
+    def build_tables(self, request_ids, max_blocks_per_seq: int, pad_block: int = 0):
+        np = self._np
+        ids = np.ascontiguousarray(request_ids, dtype=np.int64)
+        tab = np.empty((ids.shape[0], max_blocks_per_seq), np.int32)
+        lens = np.empty(ids.shape[0], np.int32)
+        self._rc(self._lib.pkv_bm_build_tables(self._h, ids.ctypes.data, ids.shape[0],
+                                               int(max_blocks_per_seq), int(pad_block),
+                                               tab.ctypes.data, lens.ctypes.data),
+                 "build_tables")
+        return tab, lens
+
+    def slots(self, request_id: int, first_pos: int, count: int):
+        np = self._np
+        out = np.empty(count, np.int32)
+        self._rc(self._lib.pkv_bm_slots(self._h, int(request_id), int(first_pos), int(count),
+                                        out.ctypes.data), "slots")
+        return out

@@ -50,7 +50,7 @@ def _compile(src: Path, verbose: bool) -> Path:
 
 def build(verbose: bool = False, jobs: int | None = None) -> Path:
     BUILD.mkdir(exist_ok=True)
-    srcs = sorted(CSRC.glob("*.hip"))
+    srcs = sorted(CSRC.glob("*.hip")) + sorted(CSRC.glob("*.cpp"))
     jobs = jobs or min(len(srcs), os.cpu_count() or 1, 16)
     with ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), srcs))

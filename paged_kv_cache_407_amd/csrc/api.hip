@@ -84,6 +84,7 @@ const char *pkv_status_string(int status) {
     case PKV_ERR_INVALID: return "invalid argument";
     case PKV_ERR_UNSUPPORTED: return "unsupported shape (head_dim 64/128, block_size 16/32)";
     case PKV_ERR_HIP: return "HIP runtime error";
+    case PKV_ERR_NO_BLOCKS: return "not enough free KV blocks";
     default: return "unknown status";
   }
 }

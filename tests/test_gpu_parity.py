@@ -444,3 +444,48 @@ def test_decode_graph_replays_match_eager():
         torch.cuda.synchronize()
         got = to_host(out)
         assert np.array_equal(got.view(np.uint32), eager.view(np.uint32)), i
+
+
+# ------------------------------------------------------- host block manager
+def test_block_manager_drives_append_and_decode():
+    """Block tables and slot mappings from the host block manager drive the
+    kernels: prompts are written through their slots, one decode step appends
+    a token per sequence (some crossing a block boundary), and the decode
+    reads the new tokens back through the manager's tables."""
+    import paged_kv_cache_407_amd as pkv
+    rng = np.random.default_rng(99)
+    Hq, Hkv, D, bs, NB = 8, 2, 128, 16, 256
+    lens = [1, 15, 16, 17, 100, 257, 33]
+    bm = pkv.BlockManager(NB - 1, bs)      # block NB-1 stays free: the pad canary
+    kc = np.full((NB, Hkv, bs, D), np.nan, np.float16)
+    vc = np.full((NB, Hkv, bs, D), np.nan, np.float16)
+    ids = list(range(len(lens)))
+    pk, pv, ps = [], [], []
+    for r, L in zip(ids, lens):
+        bm.allocate(r, L - 1)
+        pk.append(rng.standard_normal((L - 1, Hkv, D)).astype(np.float16))
+        pv.append(rng.standard_normal((L - 1, Hkv, D)).astype(np.float16))
+        ps.append(bm.slots(r, 0, L - 1))
+    pk, pv, ps = np.concatenate(pk), np.concatenate(pv), np.concatenate(ps).astype(np.int32)
+    nk = rng.standard_normal((len(ids), Hkv, D)).astype(np.float16)
+    nv = rng.standard_normal((len(ids), Hkv, D)).astype(np.float16)
+    ns = bm.append_tokens(ids)
+    MB = 20
+    tables, seq_lens = bm.build_tables(ids, MB, pad_block=NB - 1)
+    assert list(seq_lens) == lens
+    q = rng.standard_normal((len(ids), Hq, D)).astype(np.float16)
+    scale = float(np.float32(1 / np.sqrt(D)))
+
+    dk, dv = to_dev(kc), to_dev(vc)
+    pkv.kv_append(to_dev(pk), to_dev(pv), dk, dv, to_dev(ps))
+    pkv.kv_append(to_dev(nk), to_dev(nv), dk, dv, to_dev(ns))
+    out = to_host(pkv.paged_attention_decode(to_dev(q), dk, dv, to_dev(tables),
+                                             to_dev(seq_lens), max_seq_len=max(lens),
+                                             scale=scale, partition_size=64))
+    okc, ovc = oracle.kv_append(pk, pv, kc, vc, ps)
+    okc, ovc = oracle.kv_append(nk, nv, okc, ovc, ns)
+    assert np.array_equal(to_host(dk).view(np.uint16), okc.view(np.uint16))
+    ref = oracle.decode(q, okc, ovc, tables, seq_lens, scale)
+    err = max_abs(out, ref)
+    say(f"block manager end to end: max-abs {err:.3g}")
+    assert err <= TIGHT_DECODE
