@@ -51,6 +51,38 @@ __device__ __forceinline__ float xor_sum(float v, int mask) {
   return v + __shfl_xor(v, mask, kWave);
 }
 
+// IEEE maximum (NaN-propagating): lowers to v_maximum3_f32 on gfx950 with no
+// operand canonicalisation, unlike fmaxf (maxNum) on values of unknown origin
+// such as MFMA results.
+__device__ __forceinline__ float vmax(float a, float b) {
+  return __builtin_elementwise_maximum(a, b);
+}
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
+
+// Reductions over the four lanes l, l^16, l^32, l^48 with the gfx950 row
+// swaps (VALU, no LDS round trip): v_permlane32_swap exchanges the upper
+// half of one copy with the lower half of the other, so the two results hold
+// both halves' values at every lane; v_permlane16_swap does the same for odd
+// and even 16-lane rows.
+__device__ __forceinline__ float max_over_rows(float v) {
+  const unsigned u = __float_as_uint(v);
+  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  v = vmax(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const unsigned w = __float_as_uint(v);
+  const auto b = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+  return vmax(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_over_rows(float v) {
+  const unsigned u = __float_as_uint(v);
+  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const unsigned w = __float_as_uint(v);
+  const auto b = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) {
   return __builtin_amdgcn_exp2f(x);  // v_exp_f32; exp2(-inf) = 0
 }

@@ -100,55 +100,42 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p,
   const int ntiles = cdiv(kv_end, BN);
   const int32_t *trow = p.block_tables + (size_t)c * p.max_blocks_per_seq;
 
-  // The wave's query rows as B operands: column lc of block qb, dims of
-  // slot KS*g + kk (8 per slot).
-  h8_t qf[KS][2];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int qr = wq0 + 16 * qb + lc;
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (qr < qlen)
-        v = ld16(p.q + ((size_t)(q_begin + qr) * Hq + h) * D + 8 * (KS * g + kk));
-      qf[kk][qb] = as_h8(v);
-    }
-  }
-
   // Tile loader: thread owns keys KPT*lkg .. +KPT-1 and dims 8*lcc .. +7.
-  // The block id of a later tile is fetched one tile ahead and only checked
-  // where it is used: a branch on it right after its load would wait for
-  // every load issued before it (memory counters retire in order), which
-  // would stall the K/V prefetch.
-  constexpr int kNoBlock = -2147483647 - 1;
+  // It has no branches (a load under a branch makes the compiler wait for
+  // it inside the branch, serialising the tile's loads):
+  // * the block id of a later tile is read one tile ahead from a clamped
+  //   (always valid) table index and only checked where it is used; a check
+  //   right after its load would wait for every load issued before it
+  //   (memory counters retire in order);
+  // * K/V loads are unconditional (an absent key reads block 0, in bounds),
+  //   absent keys are zeroed when the tile is stored;
+  // * a block id outside the pool sets a per-thread flag, gathered once at
+  //   the end.
   const int lkg = tid % NKG, lcc = tid / NKG;
   auto lookup = [&](int t) -> int {
     const int pos = t * BN + KPT * lkg;
-    if (t >= ntiles || pos >= L) return kNoBlock;
-    return trow[pos / BS];
+    return trow[min(pos, L - 1) / BS];  // L >= 1, L <= max_blocks_per_seq * BS
   };
-  // Loads are unconditional (an absent key reads block 0, in bounds) and
-  // absent keys are zeroed when the tile is stored: a load under a branch
-  // would make the compiler wait for it inside the branch, serialising the
-  // tile's loads.
   uint4 kreg[KPT], vreg[KPT];
   unsigned live = 0;  // bit i: key i of this thread's slice exists
+  bool bad = false;   // a block id outside the pool was met
   auto load = [&](int t, int ph) {
-    if (ph != kNoBlock && (ph < 0 || ph >= p.num_blocks)) {
-      sBad = 1;
-      ph = kNoBlock;
-    }
-    live = 0;
+    // The thread's KPT keys are consecutive and share one block (BS is a
+    // multiple of KPT); the block id is only meaningful when the first of
+    // them lies below L.
+    const int pos = t * BN + KPT * lkg;
+    const bool want = t < ntiles && pos < L;
+    const bool oob = want && (ph < 0 || ph >= p.num_blocks);
+    bad |= oob;
+    const bool blk = want && !oob;
+    live = blk ? (1u << min(L - pos, KPT)) - 1u : 0u;
+    const size_t off =
+        blk ? (((size_t)ph * p.num_kv_heads + kvh) * BS + pos % BS) * D + 8 * lcc
+            : (size_t)8 * lcc;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-      const int pos = t * BN + KPT * lkg + i;
-      const bool ok = ph != kNoBlock && pos < L;
-      live |= (unsigned)ok << i;
-      const size_t off =
-          ok ? (((size_t)ph * p.num_kv_heads + kvh) * BS + pos % BS) * D + 8 * lcc
-             : (size_t)8 * lcc;
-      kreg[i] = ld16(p.k_cache + off);
-      vreg[i] = ld16(p.v_cache + off);
+      kreg[i] = ld16(p.k_cache + off + i * D);
+      vreg[i] = ld16(p.v_cache + off + i * D);
     }
   };
   auto store = [&](int buf) {
@@ -184,10 +171,25 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p,
   float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
 
   if (tid == 0) sBad = 0;
-  __syncthreads();
+  // Prologue, ordered so that only two memory latencies are exposed: the
+  // block ids of tiles 0 and 1, then the query rows (issued while the ids
+  // are in flight), then tile 0's K/V, which needs its id.
   int ph_next = lookup(0);
+  const int ph_one = lookup(1);
+  // The wave's query rows as B operands: column lc of block qb, dims of
+  // slot KS*g + kk (8 per slot).  Rows past the chunk load its last row
+  // (unconditional loads, nothing waits inside a branch); their results are
+  // never stored.
+  h8_t qf[KS][2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int qr = min(wq0 + 16 * qb + lc, qlen - 1);
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+      qf[kk][qb] = as_h8(ld16(p.q + ((size_t)(q_begin + qr) * Hq + h) * D + 8 * (KS * g + kk)));
+  }
   load(0, ph_next);
-  ph_next = lookup(1);
+  ph_next = ph_one;
   store(0);
   __syncthreads();
 
@@ -196,10 +198,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p,
   for (int kt = 0; kt < ntiles; ++kt) {
     const int buf = kt & 1;
     const int kbase = kt * BN;
-    if (kt + 1 < ntiles) {
-      load(kt + 1, ph_next);
-      ph_next = lookup(kt + 2);
-    }
+    // the next tile's loads (harmless past the last tile)
+    load(kt + 1, ph_next);
+    ph_next = lookup(kt + 2);
     // skip a tile that lies wholly above this wave's diagonal
     if (wave_live && kbase <= P + wq0 + WROWS - 1) {
       const _Float16 *Kt = sK[buf];
@@ -233,6 +234,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p,
           st[mm][1] = mfma16x16x32(fa[kk & 1][mm], qf[kk][1], st[mm][1]);
         }
       }
+
       // lane holds keys kbase + 32*(mm/2) + 8g + 4*(mm%2) + r of column lc
       const bool diag = kbase + BN - 1 > P + wq0;
       h8_t pb[2][2];
@@ -249,13 +251,12 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p,
               if (kpos > qpos) st[mm][qb][r] = -INFINITY;
             }
         }
-        float tmax = -INFINITY;
+        // the lane's 16 scores of this row, two at a time into a 3-way max
+        float tmax = st[0][qb][0];
 #pragma unroll
-        for (int mm = 0; mm < 4; ++mm)
-          tmax = fmaxf(tmax, fmaxf(fmaxf(st[mm][qb][0], st[mm][qb][1]),
-                                   fmaxf(st[mm][qb][2], st[mm][qb][3])));
-        tmax = xor_max(tmax, 16);
-        tmax = xor_max(tmax, 32);
+        for (int i = 1; i < 15; i += 2)
+          tmax = vmax3(tmax, st[i >> 2][qb][i & 3], st[(i + 1) >> 2][qb][(i + 1) & 3]);
+        tmax = max_over_rows(vmax(tmax, st[3][qb][3]));
         // Lazy rescaling: the running maximum m only moves when some row's
         // maximum exceeds it by more than 2^8, so weights stay below 256
         // (exact enough in fp16) and the O rescale is rare.  Key 0 is
@@ -284,34 +285,33 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p,
         l[qb] += psum;
       }
       // O^T[d][q] += sum_k V^T[d][k] P^T[k][q]; slot j of lane group g is key
-      // 32ks + 8g + j on both sides.
-      // V^T fragments of the first PV step are read together; each one's
-      // slot is refilled with the second step's fragment once consumed.
-      h8_t fb[DT];
+      // 32ks + 8g + j on both sides.  Step i = (ks, dt); its V^T fragment
+      // is read NFB steps ahead.
+      constexpr int NFB = 2;
+      auto read_v = [&](int i) {
+        return as_h8(ld16(&Vt[(16 * (i % DT) + lc) * VSTR + 32 * (i / DT) + 8 * g]));
+      };
+      h8_t fb[NFB];
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        fb[dt] = as_h8(ld16(&Vt[(16 * dt + lc) * VSTR + 8 * g]));
+      for (int i = 0; i < NFB; ++i) fb[i] = read_v(i);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const h8_t a = fb[dt];
-          if (ks == 0)  // fetch the second step's fragment in its place
-            fb[dt] = as_h8(ld16(&Vt[(16 * dt + lc) * VSTR + 32 + 8 * g]));
-          o[dt][0] = mfma16x16x32(a, pb[ks][0], o[dt][0]);
-          o[dt][1] = mfma16x16x32(a, pb[ks][1], o[dt][1]);
-        }
+      for (int i = 0; i < 2 * DT; ++i) {
+        const h8_t a = fb[i % NFB];
+        if (i + NFB < 2 * DT) fb[i % NFB] = read_v(i + NFB);
+        o[i % DT][0] = mfma16x16x32(a, pb[i / DT][0], o[i % DT][0]);
+        o[i % DT][1] = mfma16x16x32(a, pb[i / DT][1], o[i % DT][1]);
       }
     }
     if (kt + 1 < ntiles) store(buf ^ 1);
     __syncthreads();
   }
 
-  const bool bad = sBad != 0;
+  if (bad) sBad = 1;
+  __syncthreads();
+  const bool any_bad = sBad != 0;
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    float lt = xor_sum(l[qb], 16);
-    lt = xor_sum(lt, 32);
+    const float lt = sum_over_rows(l[qb]);
     const int qr = wq0 + 16 * qb + lc;
     if (qr < qlen) {
       float *orow = p.out + ((size_t)(q_begin + qr) * Hq + h) * D;
@@ -319,7 +319,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p,
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         f4_t r = o[dt][qb] * inv;
-        if (bad)
+        if (any_bad)
           r = f4_t{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
                    __builtin_nanf("")};
         *reinterpret_cast<f4_t *>(orow + 16 * dt + 4 * g) = r;
