@@ -63,6 +63,10 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run three plain 1 GiB device copies (the known-size "
                          "kernel that scales the HBM byte counters)")
+    ap.add_argument("--block-size-sweep", action="store_true",
+                    help="time the decode of the workload's batch at block sizes 1, 8, "
+                         "16 and 32 (same lengths and pool capacity in tokens) and "
+                         "print one JSON line per block size")
     ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH",
                                                           "COPY_WRITE"),
                     help="turn four rocprofv3 --pmc output folders (FETCH_SIZE and "
@@ -203,6 +207,9 @@ def main():
         return
     lib = pkv.load_library()
     log("library", pkv.LIB_PATH, "device", torch.cuda.get_device_name(dev))
+    if args.block_size_sweep:
+        block_size_sweep(args, dev)
+        return
 
     t0 = time.time()
     b = W.make_batch(args.workload)
@@ -399,6 +406,86 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(b, kv_bytes, args.cpu_seconds)
     print(json.dumps(line), flush=True)
+
+
+SWEEP_BLOCK_SIZES = (1, 8, 16, 32)
+
+
+def block_size_sweep(args, dev):
+    """Decode of one batch at several block sizes: the same seeded lengths,
+    queries and KV contents, the pool holding the same number of tokens
+    (num_blocks * block_size fixed), each block table as wide as the longest
+    sequence needs.  Cold caches as in the main run (replicas), per-call
+    HIP-event times with the GPU kept ahead of the host."""
+    import dataclasses
+    import torch
+    import paged_kv_cache_407_amd as pkv
+    base = W.SPECS[args.workload]
+    if base.shared_prefix or base.prefill_chunks:
+        raise SystemExit("the sweep takes a decode-only workload without sharing")
+    tokens = base.num_blocks * base.block_size
+    for bs in SWEEP_BLOCK_SIZES:
+        spec = dataclasses.replace(base, name=f"{base.name}_bs{bs}", block_size=bs,
+                                   num_blocks=tokens // bs, max_blocks_per_seq=0)
+        b = W.make_batch(spec)
+        S, Hq, D = b.q_dec.shape
+        max_len = int(b.lens_dec.max())
+        kv_bytes = W.decode_kv_bytes(b)["logical"]
+        alg = kv_bytes + b.q_dec.nbytes + S * Hq * D * 4
+        part = pkv.decode_partition_size(S, Hq, spec.num_kv_heads, D, bs, max_len,
+                                         args.partition_size)
+        wsb = pkv.decode_workspace_size(S, Hq, spec.num_kv_heads, D, bs, max_len,
+                                        args.partition_size)
+        R = max(1, min(16, math.ceil(2.0e9 / kv_bytes), int(64e9 // b.nbytes_pool())))
+
+        def to_dev(a):
+            a = np.ascontiguousarray(a)
+            if a.dtype == np.float16:
+                return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.float16)
+            return torch.from_numpy(a).to(dev)
+        nk, nv, slots = to_dev(b.new_k), to_dev(b.new_v), to_dev(b.slot_mapping)
+        tab, lens, q = to_dev(b.tables_dec), to_dev(b.lens_dec), to_dev(b.q_dec)
+        reps = []
+        for r in range(R):
+            kc, vc = to_dev(b.k_cache), to_dev(b.v_cache)
+            pkv.kv_append(nk, nv, kc, vc, slots)
+            reps.append((kc, vc, torch.empty((S, Hq, D), dtype=torch.float32, device=dev),
+                         torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None))
+
+        def call(rep):
+            kc, vc, out, ws = rep
+            pkv.paged_attention_decode(q, kc, vc, tab, lens, max_seq_len=max_len,
+                                       scale=b.scale, out=out, workspace=ws,
+                                       partition_size=args.partition_size)
+        for i in range(args.warmup):
+            call(reps[i % R])
+        n = max(args.steps, 20)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n)]
+        torch.cuda.synchronize()
+        torch.cuda._sleep(200_000_000)
+        for i, (e0, e1) in enumerate(ev):
+            e0.record()
+            call(reps[i % R])
+            e1.record()
+        torch.cuda.synchronize()
+        d = np.array([e0.elapsed_time(e1) for e0, e1 in ev]) * 1e3
+        gbs = alg / (d.mean() * 1e-6) / 1e9
+        log(f"block size {bs:2d}: decode {d.mean():8.2f} us, {gbs:7.1f} GB/s "
+            f"({100 * gbs / HBM_PEAK_GBS:5.1f} % of HBM peak), partition {part}, "
+            f"table width {b.tables_dec.shape[1]}, replicas {R}")
+        print(json.dumps({
+            "metric": "paged decode GB/s by block size", "workload": args.workload,
+            "block_size": bs, "num_blocks": spec.num_blocks,
+            "table_entries": int(sum(W.cdiv(int(L), bs) for L in b.lens_dec)),
+            "partition_size": part, "us_mean": round(float(d.mean()), 3),
+            "us_p10": round(float(np.percentile(d, 10)), 3),
+            "us_p90": round(float(np.percentile(d, 90)), 3),
+            "alg_bytes": alg, "GBps": round(gbs, 1),
+            "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "calls": n, "replicas": R}),
+            flush=True)
+        del reps
+        torch.cuda.empty_cache()
 
 
 def cpu_baseline(b: W.Batch, kv_bytes: int, budget_s: float) -> dict:

@@ -23,7 +23,8 @@
  *   seq_lens         : [num_seqs] int32, tokens held after this step's append.
  *   Query head h reads KV head h / (num_q_heads / num_kv_heads).
  *
- * Supported instances: head_dim 64 or 128, block_size 16 or 32, any
+ * Supported instances: head_dim 64 or 128; block_size 1, 8, 16 or 32 for
+ * the decode, 8, 16 or 32 for the prefill, any for kv_append; any
  * num_q_heads that is a multiple of num_kv_heads.
  *
  * Device-side contents cannot be checked without a synchronisation, so the

@@ -22,9 +22,16 @@ constexpr int kPartitionChoices[] = {1024, 512, 256};
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
-bool supported(int32_t head_dim, int32_t block_size) {
+// Compiled instances.  Decode also takes block sizes below one wave-wide
+// load (1 token per block); prefill needs a thread's 2 or 4 tile keys in
+// one block.
+bool supported_decode(int32_t head_dim, int32_t block_size) {
   return (head_dim == 64 || head_dim == 128) &&
-         (block_size == 16 || block_size == 32);
+         (block_size == 1 || block_size == 8 || block_size == 16 || block_size == 32);
+}
+bool supported_prefill(int32_t head_dim, int32_t block_size) {
+  return (head_dim == 64 || head_dim == 128) &&
+         (block_size == 8 || block_size == 16 || block_size == 32);
 }
 
 int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
@@ -82,7 +89,7 @@ const char *pkv_status_string(int status) {
   switch (status) {
     case PKV_OK: return "ok";
     case PKV_ERR_INVALID: return "invalid argument";
-    case PKV_ERR_UNSUPPORTED: return "unsupported shape (head_dim 64/128, block_size 16/32)";
+    case PKV_ERR_UNSUPPORTED: return "unsupported shape (head_dim 64/128; block_size 1/8/16/32 for decode, 8/16/32 for prefill)";
     case PKV_ERR_HIP: return "HIP runtime error";
     case PKV_ERR_NO_BLOCKS: return "not enough free KV blocks";
     default: return "unknown status";
@@ -152,7 +159,7 @@ int pkv_paged_attention_decode(float *out, const void *q, const void *k_cache,
     return PKV_ERR_INVALID;
   if ((int64_t)max_seq_len > (int64_t)max_blocks_per_seq * block_size)
     return PKV_ERR_INVALID;
-  if (!supported(head_dim, block_size)) return PKV_ERR_UNSUPPORTED;
+  if (!supported_decode(head_dim, block_size)) return PKV_ERR_UNSUPPORTED;
   const int32_t part = partition_tokens(num_seqs, num_q_heads, num_kv_heads,
                                         block_size, max_seq_len, partition_size);
   if (part <= 0) return PKV_ERR_INVALID;
@@ -208,7 +215,7 @@ int pkv_paged_attention_prefill(float *out, const void *q,
       num_q_heads % num_kv_heads || !isfinite(scale) || !(scale > 0.f))
     return PKV_ERR_INVALID;
   if (num_q_heads > 65535 || num_chunks > 65535) return PKV_ERR_INVALID;
-  if (!supported(head_dim, block_size)) return PKV_ERR_UNSUPPORTED;
+  if (!supported_prefill(head_dim, block_size)) return PKV_ERR_UNSUPPORTED;
   if (num_chunks == 0 || total_q_tokens == 0) return PKV_OK;
   if (!out || !q || !cu_q_lens || !k_cache || !v_cache || !block_tables ||
       !seq_lens)

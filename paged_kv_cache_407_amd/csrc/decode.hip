@@ -25,9 +25,11 @@
 //   tail slots may hold NaN).
 // * A sequence is cut into partitions of part_tokens (at most 64 blocks, so
 //   one VGPR holds the partition's block ids: lane j keeps entry j and a
-//   wave reads it with v_readlane).  One workgroup of 4 waves takes one
-//   (partition, sequence, head group); waves take interleaved steps of CH
-//   blocks and are merged through LDS.
+//   wave reads it with v_readlane, or, for blocks smaller than one
+//   wave-wide load, each lane fetches its token's entry with a lane
+//   permute).  One workgroup of 4 waves takes one (partition, sequence,
+//   head group); waves take interleaved steps of whole blocks and are merged
+//   through LDS.
 // * With several partitions, each workgroup stores (max, sum, unnormalised
 //   output) and decode_merge_kernel combines them: M = max_i m_i,
 //   out = sum_i 2^(m_i-M) o_i / sum_i 2^(m_i-M) l_i -- the rescaling of the
@@ -55,21 +57,29 @@ constexpr float kLazyRescale = 8.f;
 constexpr int kDecodeWaves = PKV_DECODE_WAVES;
 constexpr int kStepLoads = PKV_DECODE_STEP_LOADS;
 
+// Wave step layout.  Load i of a step that starts at block b brings token
+// b*BS + i*RPL + r to the lanes of row r.  When a block holds whole
+// wave-wide loads (BS >= RPL) every load reads one block, whose id is
+// wave-uniform; smaller blocks (SUB) put RPL/BS blocks in one load and each
+// lane fetches the id of its own token's block.
 template <int D, int BS>
 struct DecodeShape {
   static constexpr int LPR = D / 8;        // lanes per token row
   static constexpr int RPL = kWave / LPR;  // token rows per wave-wide load
-  static constexpr int LPB = BS / RPL;     // loads per lane per block
-  static constexpr int CH = LPB >= kStepLoads ? 1 : kStepLoads / LPB;  // blocks per wave step
-  static constexpr int NL = CH * LPB;      // 16-byte loads per lane per step
-  static_assert(BS % RPL == 0, "block must hold whole wave loads");
+  static constexpr bool SUB = BS < RPL;
+  static constexpr int LPB = SUB ? 1 : BS / RPL;  // loads per lane per block
+  static constexpr int NL = SUB ? kStepLoads
+                                : (LPB >= kStepLoads ? LPB : (kStepLoads / LPB) * LPB);
+  static constexpr int BPS = NL * RPL / BS;       // blocks per wave step
+  static_assert(SUB ? RPL % BS == 0 : BS % RPL == 0, "blocks and loads nest");
 };
 
 template <int D, int BS, int GH>
 __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeParams p) {
   using Sh = DecodeShape<D, BS>;
-  constexpr int LPR = Sh::LPR, RPL = Sh::RPL, LPB = Sh::LPB, CH = Sh::CH,
+  constexpr int LPR = Sh::LPR, RPL = Sh::RPL, LPB = Sh::LPB, BPS = Sh::BPS,
                 NL = Sh::NL, NW = kDecodeWaves;
+  constexpr bool SUB = Sh::SUB;
   __shared__ float s_acc[NW][GH][D];
   __shared__ float s_m[NW][GH], s_l[NW][GH];
 
@@ -131,24 +141,39 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeParams 
   const size_t head_elems = (size_t)BS * D;
   const uint4 zero = make_uint4(0, 0, 0, 0);
 
-  for (int b = blk0 + wave * CH; b < blk1; b += NW * CH) {
+  for (int b = blk0 + wave * BPS; b < blk1; b += NW * BPS) {
     uint4 kr[NL], vr[NL];
+    if constexpr (!SUB) {
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int bb = b + c;
-      const bool in = bb < blk1;
-      const int phys = __builtin_amdgcn_readlane(my_blk, in ? bb - blk0 : 0);
-      const size_t base =
-          ((size_t)phys * p.num_kv_heads + kvh) * head_elems + rrow * D + col * 8;
+      for (int c = 0; c < BPS; ++c) {
+        const int bb = b + c;
+        const bool in = bb < blk1;
+        const int phys = __builtin_amdgcn_readlane(my_blk, in ? bb - blk0 : 0);
+        const size_t base =
+            ((size_t)phys * p.num_kv_heads + kvh) * head_elems + rrow * D + col * 8;
 #pragma unroll
-      for (int j = 0; j < LPB; ++j) {
-        if (in) {
-          kr[c * LPB + j] = ld16_nt(p.k_cache + base + (size_t)j * RPL * D);
-          vr[c * LPB + j] = ld16_nt(p.v_cache + base + (size_t)j * RPL * D);
-        } else {
-          kr[c * LPB + j] = zero;
-          vr[c * LPB + j] = zero;
+        for (int j = 0; j < LPB; ++j) {
+          if (in) {
+            kr[c * LPB + j] = ld16_nt(p.k_cache + base + (size_t)j * RPL * D);
+            vr[c * LPB + j] = ld16_nt(p.v_cache + base + (size_t)j * RPL * D);
+          } else {
+            kr[c * LPB + j] = zero;
+            vr[c * LPB + j] = zero;
+          }
         }
+      }
+    } else {
+      // Per-lane block ids from the lanes that hold them; a token past the
+      // partition reads entry 0's block (in bounds) and is masked below.
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        const int tok = b * BS + i * RPL + rrow;
+        const int bl = tok / BS - blk0;
+        const int phys = __shfl(my_blk, bl < blk1 - blk0 ? bl : 0, kWave);
+        const size_t off = ((size_t)phys * p.num_kv_heads + kvh) * head_elems +
+                           (size_t)(tok % BS) * D + col * 8;
+        kr[i] = ld16_nt(p.k_cache + off);
+        vr[i] = ld16_nt(p.v_cache + off);
       }
     }
 #pragma unroll
@@ -157,7 +182,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeParams 
       float cmax = -INFINITY;
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
-        const int tok = (b + i / LPB) * BS + (i % LPB) * RPL + rrow;
+        const int tok = b * BS + i * RPL + rrow;
         const float d = group_sum<LPR>(dot8(qv[g], as_h8(kr[i]), 0.f));
         sc[i] = tok < tok_end ? d * p.scale_log2e : -INFINITY;
         cmax = fmaxf(cmax, sc[i]);
@@ -172,7 +197,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeParams 
       for (int k = 0; k < 8; ++k) acc[g][k] *= alpha;
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
-        const int tok = (b + i / LPB) * BS + (i % LPB) * RPL + rrow;
+        const int tok = b * BS + i * RPL + rrow;
         const bool ok = tok < tok_end;
         const float pr = ok ? fast_exp2(sc[i] - mnew) : 0.f;
         const h8_t v = as_h8(ok ? vr[i] : zero);
@@ -499,7 +524,8 @@ static hipError_t launch(const DecodeParams &p, hipStream_t stream) {
       (int64_t)p.num_parts * p.num_seqs * (p.num_q_heads / GH);
   if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  if constexpr (GH == 8)
+  // the grouped kernel steps over whole blocks of whole wave-wide loads
+  if constexpr (GH == 8 && !DecodeShape<D, BS>::SUB)
     decode_gqa8_kernel<D, BS><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(p);
   else
     decode_kernel<D, BS, GH>
@@ -527,10 +553,21 @@ hipError_t launch_decode(const DecodeParams &p, int head_dim, int block_size,
       p.part_tokens > kMaxPartBlocks * block_size || p.group <= 0 ||
       p.num_q_heads % p.group)
     return hipErrorInvalidValue;
-  if (head_dim == 128 && block_size == 16) return launch_heads<128, 16>(p, stream);
-  if (head_dim == 128 && block_size == 32) return launch_heads<128, 32>(p, stream);
-  if (head_dim == 64 && block_size == 16) return launch_heads<64, 16>(p, stream);
-  if (head_dim == 64 && block_size == 32) return launch_heads<64, 32>(p, stream);
+  if (head_dim == 128) {
+    switch (block_size) {
+      case 1: return launch_heads<128, 1>(p, stream);
+      case 8: return launch_heads<128, 8>(p, stream);
+      case 16: return launch_heads<128, 16>(p, stream);
+      case 32: return launch_heads<128, 32>(p, stream);
+    }
+  } else if (head_dim == 64) {
+    switch (block_size) {
+      case 1: return launch_heads<64, 1>(p, stream);
+      case 8: return launch_heads<64, 8>(p, stream);
+      case 16: return launch_heads<64, 16>(p, stream);
+      case 32: return launch_heads<64, 32>(p, stream);
+    }
+  }
   return hipErrorInvalidValue;
 }
 

@@ -341,8 +341,10 @@ static hipError_t launch(const PrefillParams &p, int max_q_len,
 
 hipError_t launch_prefill(const PrefillParams &p, int head_dim, int block_size,
                           int max_q_len, hipStream_t stream) {
+  if (head_dim == 128 && block_size == 8) return launch<128, 8>(p, max_q_len, stream);
   if (head_dim == 128 && block_size == 16) return launch<128, 16>(p, max_q_len, stream);
   if (head_dim == 128 && block_size == 32) return launch<128, 32>(p, max_q_len, stream);
+  if (head_dim == 64 && block_size == 8) return launch<64, 8>(p, max_q_len, stream);
   if (head_dim == 64 && block_size == 16) return launch<64, 16>(p, max_q_len, stream);
   if (head_dim == 64 && block_size == 32) return launch<64, 32>(p, max_q_len, stream);
   return hipErrorInvalidValue;

@@ -91,7 +91,8 @@ def test_invalid_arguments_are_rejected_on_the_host():
     assert dec(P, P, P, P, P, P, 2, 6, 4, 128, 16, 8, 4, 64, 0.1, 0, None, 0, None) == 1
     # unsupported head_dim / block size
     assert dec(P, P, P, P, P, P, 2, 4, 4, 96, 16, 8, 4, 64, 0.1, 0, None, 0, None) == 2
-    assert dec(P, P, P, P, P, P, 2, 4, 4, 128, 8, 8, 8, 64, 0.1, 0, None, 0, None) == 2
+    assert dec(P, P, P, P, P, P, 2, 4, 4, 128, 4, 8, 16, 64, 0.1, 0, None, 0, None) == 2
+    assert dec(P, P, P, P, P, P, 2, 4, 4, 128, 2, 8, 32, 64, 0.1, 0, None, 0, None) == 2
     # max_seq_len beyond the table
     assert dec(P, P, P, P, P, P, 2, 4, 4, 128, 16, 8, 4, 65, 0.1, 0, None, 0, None) == 1
     # split needed but no workspace
@@ -103,6 +104,8 @@ def test_invalid_arguments_are_rejected_on_the_host():
     pre = lib.pkv_paged_attention_prefill
     assert pre(P, P, P, P, P, P, P, 1, 8, 8, 4, 3, 128, 16, 8, 4, 0.1, None) == 1
     assert pre(P, P, P, P, P, P, P, 1, 8, 8, 4, 4, 80, 16, 8, 4, 0.1, None) == 2
+    # block size 1 is a decode-only instance
+    assert pre(P, P, P, P, P, P, P, 1, 8, 8, 4, 4, 128, 1, 8, 4, 0.1, None) == 2
     assert pre(P, P, P, P, P, P, P, 1, 8, 8, 4, 4, 128, 16, 8, 4, -1.0, None) == 1
     assert pre(None, None, None, None, None, None, None, 0, 0, 0, 4, 4, 128, 16, 8, 4, 0.1, None) == 0
 

@@ -44,6 +44,13 @@ SMALL_DECODE = [
     gpu_spec("d64_bs32_gqa2", 4, 2, 64, 32, EDGE_LENS, seed=4),
     gpu_spec("d128_bs16_gqa4", 8, 2, 128, 16, EDGE_LENS, seed=5),
     gpu_spec("d128_bs32_gqa8", 16, 2, 128, 32, EDGE_LENS, seed=6),
+    # block sizes below one wave-wide load (per-lane block ids) and block
+    # size 8, for the decode's block-size sweep
+    gpu_spec("d128_bs1_mha", 4, 4, 128, 1, EDGE_LENS, seed=7),
+    gpu_spec("d64_bs1_gqa8", 8, 1, 64, 1, EDGE_LENS, seed=8),
+    gpu_spec("d128_bs8_gqa2", 4, 2, 128, 8, EDGE_LENS, seed=9),
+    gpu_spec("d128_bs8_gqa8", 16, 2, 128, 8, EDGE_LENS, seed=10),
+    gpu_spec("d64_bs8_mha", 4, 4, 64, 8, EDGE_LENS, seed=16),
 ]
 
 
@@ -250,11 +257,12 @@ def test_decode_empty_batch():
 
 # -------------------------------------------------------------------- prefill
 def pf_spec(name, Hq, Hkv, D, bs, chunk, prefix_hi, n_chunks=3, seed=0):
+    mb = max(40, W.cdiv(600, bs), W.cdiv(chunk + prefix_hi, bs))
     return W.Spec(name=name, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, block_size=bs,
-                  num_blocks=n_chunks * W.cdiv(chunk + prefix_hi, bs) + 4 * 40 + 9,
+                  num_blocks=n_chunks * W.cdiv(chunk + prefix_hi, bs) + 4 * mb + 9,
                   seed=seed, decode_count=4, decode_dist="uniform", decode_lo=1,
                   decode_hi=600, prefill_chunks=n_chunks, prefill_chunk_len=chunk,
-                  prefill_prefix_lo=0, prefill_prefix_hi=prefix_hi, max_blocks_per_seq=40)
+                  prefill_prefix_lo=0, prefill_prefix_hi=prefix_hi, max_blocks_per_seq=mb)
 
 
 SMALL_PREFILL = [
@@ -263,6 +271,8 @@ SMALL_PREFILL = [
     pf_spec("pf_d64_bs16", 4, 4, 64, 16, 1, 300, seed=13),
     pf_spec("pf_d64_bs32", 4, 1, 64, 32, 129, 0, seed=14),
     pf_spec("pf_d128_bs16_long", 2, 2, 128, 16, 300, 300, seed=15),
+    pf_spec("pf_d128_bs8_gqa", 4, 2, 128, 8, 100, 200, seed=17),
+    pf_spec("pf_d64_bs8", 4, 4, 64, 8, 130, 70, seed=18),
 ]
 
 
