@@ -67,6 +67,11 @@ def parse():
                     help="time the decode of the workload's batch at block sizes 1, 8, "
                          "16 and 32 (same lengths and pool capacity in tokens) and "
                          "print one JSON line per block size")
+    ap.add_argument("--swap-bench", action="store_true",
+                    help="time swapping blocks of the workload's shape out to a pinned "
+                         "host pool and back (kernel and DMA paths); one JSON line per "
+                         "direction and path")
+    ap.add_argument("--swap-blocks", type=int, default=1024)
     ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH",
                                                           "COPY_WRITE"),
                     help="turn four rocprofv3 --pmc output folders (FETCH_SIZE and "
@@ -209,6 +214,9 @@ def main():
     log("library", pkv.LIB_PATH, "device", torch.cuda.get_device_name(dev))
     if args.block_size_sweep:
         block_size_sweep(args, dev)
+        return
+    if args.swap_bench:
+        swap_bench(args, dev)
         return
 
     t0 = time.time()
@@ -486,6 +494,57 @@ def block_size_sweep(args, dev):
             flush=True)
         del reps
         torch.cuda.empty_cache()
+
+
+def swap_bench(args, dev):
+    """Swap-out (device pool -> pinned host pool) and swap-in (back) of
+    ``--swap-blocks`` blocks scattered over the workload's device pool, to
+    consecutive host blocks and back to other scattered device blocks: the
+    kernel path (device id lists, one launch) and the DMA path (host id
+    lists, hipMemcpyAsync per run).  Bytes = blocks x 2 (K, V) x Hkv x bs x
+    D x 2 each way; the host link bounds both."""
+    import torch
+    import paged_kv_cache_407_amd as pkv
+    spec = W.SPECS[args.workload]
+    NB, Hkv, bs, D = spec.num_blocks, spec.num_kv_heads, spec.block_size, spec.head_dim
+    n = min(args.swap_blocks, NB)
+    rng = np.random.default_rng(1)
+    dk = torch.randn((NB, Hkv, bs, D), device=dev).half()
+    dv = torch.randn((NB, Hkv, bs, D), device=dev).half()
+    hk = torch.empty((n, Hkv, bs, D), dtype=torch.float16, pin_memory=True)
+    hv = torch.empty((n, Hkv, bs, D), dtype=torch.float16, pin_memory=True)
+    out_src = rng.permutation(NB)[:n].astype(np.int32)
+    in_dst = rng.permutation(NB)[:n].astype(np.int32)
+    host = np.arange(n, dtype=np.int32)
+    ids = {k: torch.from_numpy(v).to(dev) for k, v in
+           (("out_src", out_src), ("in_dst", in_dst), ("host", host))}
+    nbytes = n * 2 * Hkv * bs * D * 2
+    cases = [
+        ("out", "kernel", lambda: pkv.copy_blocks(dk, dv, hk, hv, ids["out_src"], ids["host"])),
+        ("in", "kernel", lambda: pkv.copy_blocks(hk, hv, dk, dv, ids["host"], ids["in_dst"])),
+        ("out", "dma", lambda: pkv.copy_blocks_dma(dk, dv, hk, hv, out_src, host)),
+        ("in", "dma", lambda: pkv.copy_blocks_dma(hk, hv, dk, dv, host, in_dst)),
+    ]
+    for direction, path, fn in cases:
+        for _ in range(max(args.warmup, 1)):
+            fn()
+        torch.cuda.synchronize()
+        reps = max(3, min(args.steps, 20))
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for e0, e1 in ev:
+            e0.record()
+            fn()
+            e1.record()
+        torch.cuda.synchronize()
+        d = np.array([e0.elapsed_time(e1) for e0, e1 in ev]) * 1e3
+        gbs = nbytes / (d.mean() * 1e-6) / 1e9
+        log(f"swap {direction:3s} {path:6s}: {n} blocks, {nbytes / 1e6:.1f} MB, "
+            f"{d.mean():9.1f} us, {gbs:6.1f} GB/s")
+        print(json.dumps({"metric": "KV block swap GB/s", "direction": direction,
+                          "path": path, "workload": args.workload, "blocks": n,
+                          "bytes": nbytes, "us_mean": round(float(d.mean()), 1),
+                          "GBps": round(gbs, 2), "calls": reps}), flush=True)
 
 
 def cpu_baseline(b: W.Batch, kv_bytes: int, budget_s: float) -> dict:

@@ -215,6 +215,53 @@ int pkv_bm_build_tables(const pkv_block_manager *bm, const int64_t *request_ids,
  * must already hold them), e.g. the slot_mapping of a prompt's prefill. */
 int pkv_bm_slots(const pkv_block_manager *bm, int64_t request_id,
                  int32_t first_pos, int32_t count, int32_t *slots);
+/* Moves a request from one manager to another ("LLM 推理引擎 …", §4.4 Swap:
+ * a preempted request's KV goes from GPU blocks to CPU blocks and later
+ * back).  The target takes ceil(len / block_size) blocks for the request's
+ * tokens (its length carries over), the source releases the request's
+ * blocks (a block shared with another request stays held by it).
+ * src_blocks[i] -> dst_blocks[i], i < *count, is the copy the caller must
+ * enqueue (pkv_copy_blocks / pkv_copy_blocks_dma) before anything reuses the
+ * released source blocks.  Both managers must have the same block_size;
+ * capacity must cover the request's block count.  PKV_ERR_NO_BLOCKS (and
+ * nothing changed) when the target has too few free blocks. */
+int pkv_bm_swap(pkv_block_manager *from, pkv_block_manager *to, int64_t request_id,
+                int32_t *src_blocks, int32_t *dst_blocks, int32_t capacity,
+                int32_t *count);
+
+/*
+ * Block copies between two KV pools ("LLM 推理引擎 …", §4.4 Swap: the
+ * device-to-host copy of a swapped-out request's blocks and the
+ * host-to-device copy that brings it back).  For i < count, block
+ * src_blocks[i] of (src_k, src_v) is copied, bit for bit, to block
+ * dst_blocks[i] of (dst_k, dst_v); a block is num_kv_heads * block_size *
+ * head_dim fp16 of K and as many of V, contiguous in either pool (the cache
+ * layout above).  A pool is device memory or pinned host memory (allocated
+ * pinned, e.g. hipHostMalloc; a pool in pinned host memory is read and
+ * written over the host link).  Ownership stays with the caller.
+ * Destination blocks must be distinct and must not be source blocks of the
+ * same call in the same pool (such copies race).
+ *
+ * pkv_copy_blocks: one kernel launch; src_blocks / dst_blocks are device or
+ * pinned host arrays, read by the kernel; a pair with an id outside its
+ * pool is skipped.  Pageable host memory anywhere -> PKV_ERR_INVALID.
+ * pkv_copy_blocks_dma: src_blocks / dst_blocks are host arrays read before
+ * return; runs of blocks consecutive on both sides become one
+ * hipMemcpyAsync each for K and for V (the DMA engines); any id outside its
+ * pool -> PKV_ERR_INVALID before anything is enqueued.
+ * Both: head_dim a multiple of 8, 16-byte aligned pools (kernel path).
+ */
+int pkv_copy_blocks(const void *src_k, const void *src_v, void *dst_k, void *dst_v,
+                    const int32_t *src_blocks, const int32_t *dst_blocks,
+                    int32_t count, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t block_size, int32_t src_num_blocks,
+                    int32_t dst_num_blocks, void *stream);
+int pkv_copy_blocks_dma(const void *src_k, const void *src_v, void *dst_k,
+                        void *dst_v, const int32_t *src_blocks,
+                        const int32_t *dst_blocks, int32_t count,
+                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                        int32_t src_num_blocks, int32_t dst_num_blocks,
+                        void *stream);
 
 #ifdef __cplusplus
 }

@@ -22,7 +22,7 @@ LIB_PATH = _HERE / "liboracle.so"
 SOURCE_PATH = _HERE / "oracle.c"
 
 _ERRORS = {1: "bad argument", 2: "slot or block id out of range",
-           3: "duplicate slot", 4: "out of memory"}
+           3: "duplicate slot or destination block", 4: "out of memory"}
 
 
 def _ptr(a: np.ndarray):
@@ -61,6 +61,8 @@ class Oracle:
         lib.oracle_prefill.argtypes = [P, P, P, P, P, P, I32, P, I32, I32, I32,
                                        I32, I32, I32, D, P, I64]
         lib.oracle_prefill.restype = ctypes.c_int
+        lib.oracle_copy_blocks.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, I32, I32]
+        lib.oracle_copy_blocks.restype = ctypes.c_int
         self.lib = lib
         self.path = path
 
@@ -132,6 +134,24 @@ class Oracle:
         return out
 
 
+    def copy_blocks(self, src_k, src_v, dst_k, dst_v, src_blocks, dst_blocks):
+        """Copies of the destination pools with block src_blocks[i] of the
+        source pools written to block dst_blocks[i]; returns (dst_k, dst_v)."""
+        sk, sv = _c(src_k, np.float16), _c(src_v, np.float16)
+        dk = np.array(dst_k, dtype=np.float16, copy=True, order="C")
+        dv = np.array(dst_v, dtype=np.float16, copy=True, order="C")
+        s, d = _c(src_blocks, np.int32), _c(dst_blocks, np.int32)
+        sNB, Hkv, bs, D = sk.shape
+        dNB = dk.shape[0]
+        if sv.shape != sk.shape or dv.shape != dk.shape or dk.shape[1:] != sk.shape[1:] \
+                or s.shape != d.shape or s.ndim != 1:
+            raise ValueError("shape mismatch")
+        rc = self.lib.oracle_copy_blocks(_ptr(sk), _ptr(sv), _ptr(dk), _ptr(dv), _ptr(s),
+                                         _ptr(d), s.shape[0], Hkv, D, bs, sNB, dNB)
+        self._check(rc, "copy_blocks")
+        return dk, dv
+
+
 _default: Oracle | None = None
 
 
@@ -156,3 +176,7 @@ def decode(*a, **k):
 
 def prefill(*a, **k):
     return get().prefill(*a, **k)
+
+
+def copy_blocks(*a, **k):
+    return get().copy_blocks(*a, **k)

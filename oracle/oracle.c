@@ -26,6 +26,10 @@
  *                  tokens has absolute position P + j and sees keys 0..P+j
  *                  (same page, §4.3 Chunked Prefill; the causal rule of the
  *                  prefill phase in §1.1).
+ *   block copy  -- swapping moves a request's KV from its GPU blocks to CPU
+ *                  blocks and back (same page, §4.4 Swap): every element of
+ *                  a source block, all KV heads and positions, K and V, is
+ *                  copied to the paired destination block.
  *
  * Softmax is computed in two passes (maximum first, then exponentials),
  * deliberately not with the GPU's running-max recurrence.
@@ -111,6 +115,50 @@ int oracle_kv_append(const uint16_t *key, const uint16_t *value,
                 v_cache[dst] = value[src];
             }
         }
+    }
+    return 0;
+}
+
+/* For i < count: block src_blocks[i] of (src_k, src_v) -> block dst_blocks[i]
+ * of (dst_k, dst_v), element by element.  Pools [nb][num_kv_heads]
+ * [block_size][head_dim] fp16 bits.  An id outside its pool is an error (2),
+ * a destination named twice is an error (3). */
+int oracle_copy_blocks(const uint16_t *src_k, const uint16_t *src_v,
+                       uint16_t *dst_k, uint16_t *dst_v,
+                       const int32_t *src_blocks, const int32_t *dst_blocks,
+                       int32_t count, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t block_size, int32_t src_num_blocks,
+                       int32_t dst_num_blocks)
+{
+    if (count < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+        src_num_blocks <= 0 || dst_num_blocks <= 0)
+        return 1;
+    unsigned char *seen = calloc((size_t)dst_num_blocks, 1);
+    if (!seen)
+        return 4;
+    for (int32_t i = 0; i < count; i++) {
+        int32_t s = src_blocks[i], d = dst_blocks[i];
+        if (s < 0 || s >= src_num_blocks || d < 0 || d >= dst_num_blocks) {
+            free(seen);
+            return 2;
+        }
+        if (seen[d]) {
+            free(seen);
+            return 3;
+        }
+        seen[d] = 1;
+    }
+    free(seen);
+    for (int32_t i = 0; i < count; i++) {
+        int64_t s = src_blocks[i], d = dst_blocks[i];
+        for (int32_t h = 0; h < num_kv_heads; h++)
+            for (int32_t o = 0; o < block_size; o++)
+                for (int32_t e = 0; e < head_dim; e++) {
+                    int64_t from = ((s * num_kv_heads + h) * block_size + o) * head_dim + e;
+                    int64_t to = ((d * num_kv_heads + h) * block_size + o) * head_dim + e;
+                    dst_k[to] = src_k[from];
+                    dst_v[to] = src_v[from];
+                }
     }
     return 0;
 }

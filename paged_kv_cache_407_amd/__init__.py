@@ -48,6 +48,11 @@ SIGNATURES = {
     "pkv_bm_block_table": (_I32, [_P, _I64, _P, _I32]),
     "pkv_bm_build_tables": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _P, _P]),
     "pkv_bm_slots": (ctypes.c_int, [_P, _I64, _I32, _I32, _P]),
+    "pkv_bm_swap": (ctypes.c_int, [_P, _P, _I64, _P, _P, _I32, _P]),
+    "pkv_copy_blocks": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
+                                       _I32, _P]),
+    "pkv_copy_blocks_dma": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32,
+                                           _I32, _I32, _P]),
 }
 PKV_ERR_NO_BLOCKS = 4
 
@@ -204,6 +209,62 @@ def paged_attention_prefill(q, cu_q_lens, k_cache, v_cache, block_tables, seq_le
     return out
 
 
+def _pool(t: torch.Tensor, name: str):
+    """A KV pool [NB, Hkv, bs, D] fp16 on the GPU or in pinned host memory."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type == "cpu" and not t.is_pinned():
+        raise ValueError(f"{name} on the host must be pinned (pin_memory=True)")
+    if t.device.type not in ("cpu", "cuda"):
+        raise ValueError(f"{name} must be on the GPU or in pinned host memory")
+    if t.dtype != torch.float16 or t.dim() != 4 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous [NB, Hkv, bs, D] float16 tensor")
+    return tuple(t.shape)
+
+
+def _pools(src_k, src_v, dst_k, dst_v):
+    s, sv, d, dv = (_pool(src_k, "src_k"), _pool(src_v, "src_v"), _pool(dst_k, "dst_k"),
+                    _pool(dst_v, "dst_v"))
+    if s != sv or d != dv or s[1:] != d[1:]:
+        raise ValueError("pools must share [Hkv, bs, D] and K/V shapes must match")
+    return s[0], d[0], s[1], s[2], s[3]
+
+
+def copy_blocks(src_k, src_v, dst_k, dst_v, src_blocks, dst_blocks, stream=None):
+    """Copies block src_blocks[i] of (src_k, src_v) to block dst_blocks[i] of
+    (dst_k, dst_v) in one kernel; pools on the GPU or in pinned host memory,
+    block lists int32 on the GPU (or pinned).  Ids outside a pool are
+    skipped."""
+    sNB, dNB, Hkv, bs, D = _pools(src_k, src_v, dst_k, dst_v)
+    for t, n in ((src_blocks, "src_blocks"), (dst_blocks, "dst_blocks")):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.int32 or t.dim() != 1 \
+                or not t.is_contiguous() or (t.device.type == "cpu" and not t.is_pinned()):
+            raise ValueError(f"{n} must be a contiguous int32 vector on the GPU or pinned")
+    if src_blocks.shape != dst_blocks.shape:
+        raise ValueError("src_blocks and dst_blocks differ in length")
+    rc = load_library().pkv_copy_blocks(src_k.data_ptr(), src_v.data_ptr(), dst_k.data_ptr(),
+                                        dst_v.data_ptr(), src_blocks.data_ptr(),
+                                        dst_blocks.data_ptr(), src_blocks.shape[0], Hkv, D, bs,
+                                        sNB, dNB, _stream(stream))
+    _check(rc, "copy_blocks")
+
+
+def copy_blocks_dma(src_k, src_v, dst_k, dst_v, src_blocks, dst_blocks, stream=None):
+    """The same copy as ``copy_blocks`` with host-side block lists (any int
+    sequence), issued as hipMemcpyAsync per run of consecutive blocks."""
+    import numpy as np
+    sNB, dNB, Hkv, bs, D = _pools(src_k, src_v, dst_k, dst_v)
+    s = np.ascontiguousarray(src_blocks, dtype=np.int32)
+    d = np.ascontiguousarray(dst_blocks, dtype=np.int32)
+    if s.shape != d.shape or s.ndim != 1:
+        raise ValueError("src_blocks and dst_blocks must be 1-D of equal length")
+    rc = load_library().pkv_copy_blocks_dma(src_k.data_ptr(), src_v.data_ptr(),
+                                            dst_k.data_ptr(), dst_v.data_ptr(), s.ctypes.data,
+                                            d.ctypes.data, s.shape[0], Hkv, D, bs, sNB, dNB,
+                                            _stream(stream))
+    _check(rc, "copy_blocks_dma")
+
+
 class OutOfBlocks(PkvError):
     """The block manager has too few free blocks (nothing was changed)."""
 
@@ -296,3 +357,15 @@ class BlockManager:
         self._rc(self._lib.pkv_bm_slots(self._h, int(request_id), int(first_pos), int(count),
                                         out.ctypes.data), "slots")
         return out
+
+    def swap_to(self, other: "BlockManager", request_id: int):
+        """Moves a request to ``other`` (e.g. the host pool's manager on swap
+        out, the device pool's on swap in); returns the (source, target)
+        block pairs the caller must copy before reusing the source blocks."""
+        np = self._np
+        n = max(len(self.block_table(request_id)), 1)
+        src, dst = np.empty(n, np.int32), np.empty(n, np.int32)
+        cnt = ctypes.c_int32()
+        self._rc(self._lib.pkv_bm_swap(self._h, other._h, int(request_id), src.ctypes.data,
+                                       dst.ctypes.data, n, ctypes.byref(cnt)), "swap")
+        return src[:cnt.value], dst[:cnt.value]

@@ -83,6 +83,37 @@ int hip_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_HIP; }
 
 }  // namespace
 
+namespace {
+
+// A pool argument as the kernel must address it: device memory as is,
+// pinned host memory through its device mapping; anything else (pageable
+// host memory) cannot be reached by a kernel.
+bool kernel_address(const void *p, const void **out) {
+  hipPointerAttribute_t a;
+  if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+    (void)hipGetLastError();  // an unknown pointer is not a launch failure
+    return false;
+  }
+  if (a.type == hipMemoryTypeDevice || a.type == hipMemoryTypeManaged) {
+    *out = p;
+    return true;
+  }
+  if (a.type == hipMemoryTypeHost && a.devicePointer) {
+    *out = (const char *)a.devicePointer +
+           ((const char *)p - (const char *)(a.hostPointer ? a.hostPointer : p));
+    return true;
+  }
+  return false;
+}
+
+bool copy_shape_ok(int32_t count, int32_t num_kv_heads, int32_t head_dim,
+                   int32_t block_size, int32_t src_num_blocks, int32_t dst_num_blocks) {
+  return count >= 0 && num_kv_heads > 0 && head_dim > 0 && head_dim % 8 == 0 &&
+         block_size > 0 && src_num_blocks > 0 && dst_num_blocks > 0;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char *pkv_status_string(int status) {
@@ -241,6 +272,74 @@ int pkv_paged_attention_prefill(float *out, const void *q,
   p.scale_log2e = scale * kLog2e;
   return hip_status(launch_prefill(p, head_dim, block_size, max_q_len,
                                    (hipStream_t)stream));
+}
+
+
+int pkv_copy_blocks(const void *src_k, const void *src_v, void *dst_k, void *dst_v,
+                    const int32_t *src_blocks, const int32_t *dst_blocks,
+                    int32_t count, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t block_size, int32_t src_num_blocks,
+                    int32_t dst_num_blocks, void *stream) {
+  if (!copy_shape_ok(count, num_kv_heads, head_dim, block_size, src_num_blocks,
+                     dst_num_blocks))
+    return PKV_ERR_INVALID;
+  if (count == 0) return PKV_OK;
+  if (!src_k || !src_v || !dst_k || !dst_v || !src_blocks || !dst_blocks)
+    return PKV_ERR_INVALID;
+  if (!aligned16(src_k) || !aligned16(src_v) || !aligned16(dst_k) || !aligned16(dst_v))
+    return PKV_ERR_INVALID;
+  const void *a[6];
+  const void *in[6] = {src_k, src_v, dst_k, dst_v, src_blocks, dst_blocks};
+  for (int i = 0; i < 6; ++i)
+    if (!kernel_address(in[i], &a[i])) return PKV_ERR_INVALID;
+  CopyParams p;
+  p.src_k = (const uint4 *)a[0];
+  p.src_v = (const uint4 *)a[1];
+  p.dst_k = (uint4 *)a[2];
+  p.dst_v = (uint4 *)a[3];
+  p.src_ids = (const int32_t *)a[4];
+  p.dst_ids = (const int32_t *)a[5];
+  p.count = count;
+  p.src_num_blocks = src_num_blocks;
+  p.dst_num_blocks = dst_num_blocks;
+  p.chunks_per_block = (int64_t)num_kv_heads * block_size * head_dim / 8;
+  return hip_status(launch_copy_blocks(p, (hipStream_t)stream));
+}
+
+int pkv_copy_blocks_dma(const void *src_k, const void *src_v, void *dst_k,
+                        void *dst_v, const int32_t *src_blocks,
+                        const int32_t *dst_blocks, int32_t count,
+                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                        int32_t src_num_blocks, int32_t dst_num_blocks,
+                        void *stream) {
+  if (!copy_shape_ok(count, num_kv_heads, head_dim, block_size, src_num_blocks,
+                     dst_num_blocks))
+    return PKV_ERR_INVALID;
+  if (count == 0) return PKV_OK;
+  if (!src_k || !src_v || !dst_k || !dst_v || !src_blocks || !dst_blocks)
+    return PKV_ERR_INVALID;
+  for (int32_t i = 0; i < count; ++i)
+    if (src_blocks[i] < 0 || src_blocks[i] >= src_num_blocks || dst_blocks[i] < 0 ||
+        dst_blocks[i] >= dst_num_blocks)
+      return PKV_ERR_INVALID;
+  const size_t bytes = (size_t)num_kv_heads * block_size * head_dim * 2;
+  hipStream_t st = (hipStream_t)stream;
+  for (int32_t i = 0; i < count;) {
+    // one copy per run of blocks consecutive on both sides
+    int32_t n = 1;
+    while (i + n < count && src_blocks[i + n] == src_blocks[i] + n &&
+           dst_blocks[i + n] == dst_blocks[i] + n)
+      ++n;
+    const size_t so = (size_t)src_blocks[i] * bytes, dof = (size_t)dst_blocks[i] * bytes;
+    hipError_t e = hipMemcpyAsync((char *)dst_k + dof, (const char *)src_k + so,
+                                  n * bytes, hipMemcpyDefault, st);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync((char *)dst_v + dof, (const char *)src_v + so, n * bytes,
+                         hipMemcpyDefault, st);
+    if (e != hipSuccess) return PKV_ERR_HIP;
+    i += n;
+  }
+  return PKV_OK;
 }
 
 }  // extern "C"

@@ -16,6 +16,11 @@
 // free list.  Only full blocks are shared, and a request never appends into
 // a full block, so a shared block is never written after it is shared.
 //
+// Swapping (same page, §4.4) pairs two managers, one over the device pool
+// and one over a host pool: moving a request from one to the other takes
+// blocks for its tokens in the target, releases its blocks in the source and
+// reports the (source, target) block pairs for the copy.
+//
 // Plain host code (no device calls), not thread-safe.
 #include <stdint.h>
 
@@ -188,6 +193,32 @@ int pkv_bm_slots(const pkv_block_manager *bm, int64_t request_id,
     const int32_t p = first_pos + i;
     slots[i] = it->second.blocks[p / bs] * bs + p % bs;
   }
+  return PKV_OK;
+}
+
+int pkv_bm_swap(pkv_block_manager *from, pkv_block_manager *to, int64_t request_id,
+                int32_t *src_blocks, int32_t *dst_blocks, int32_t capacity,
+                int32_t *count) {
+  if (!from || !to || from == to || !count || capacity < 0 ||
+      from->block_size != to->block_size)
+    return PKV_ERR_INVALID;
+  auto it = from->seqs.find(request_id);
+  if (it == from->seqs.end() || to->find(request_id)) return PKV_ERR_INVALID;
+  const std::vector<int32_t> &held = it->second.blocks;
+  const int32_t n = (int32_t)held.size();
+  if (n > capacity || (n && (!src_blocks || !dst_blocks))) return PKV_ERR_INVALID;
+  if ((int32_t)to->free_list.size() < n) return PKV_ERR_NO_BLOCKS;
+  pkv_block_manager::Seq moved;
+  moved.len = it->second.len;
+  for (int32_t i = 0; i < n; ++i) {
+    moved.blocks.push_back(to->take());
+    src_blocks[i] = held[i];
+    dst_blocks[i] = moved.blocks[i];
+  }
+  to->seqs.emplace(request_id, std::move(moved));
+  for (int32_t b : held) from->release(b);  // shared blocks stay with their other owners
+  from->seqs.erase(it);
+  *count = n;
   return PKV_OK;
 }
 

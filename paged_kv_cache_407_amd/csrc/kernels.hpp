@@ -46,6 +46,15 @@ struct PrefillParams {
 };
 
 hipError_t launch_kv_append(const AppendParams &p, hipStream_t stream);
+
+struct CopyParams {
+  const uint4 *src_k, *src_v;  // [src_num_blocks][chunks_per_block]
+  uint4 *dst_k, *dst_v;        // [dst_num_blocks][chunks_per_block]
+  const int32_t *src_ids, *dst_ids;  // [count], device-accessible
+  int32_t count, src_num_blocks, dst_num_blocks;
+  int64_t chunks_per_block;    // num_kv_heads * block_size * head_dim / 8
+};
+hipError_t launch_copy_blocks(const CopyParams &p, hipStream_t stream);
 // D in {64,128}, BS in {16,32}; returns hipErrorInvalidValue otherwise.
 // part_tokens must be a multiple of BS and at most kMaxPartBlocks * BS.
 constexpr int kMaxPartBlocks = 64;

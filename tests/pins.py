@@ -369,9 +369,51 @@ def pin_append_roundtrip(orc, spec):
     assert np.array_equal(before, after), "untouched slots changed"
 
 
+def pin_swap(orc, spec, seed=5):
+    """Swapping ("LLM 推理引擎 …", §4.4: a request's KV goes from its GPU
+    blocks to CPU blocks and back) must keep every token's K and V at its
+    logical position: after copying each sequence's blocks to shuffled blocks
+    of a second pool, decoding through the rewritten tables gives the dense
+    attention over the generator's logical-order rows; the second pool's
+    other blocks keep their bits; copying the blocks back to fresh positions
+    of a third pool gives the same decode, bit for bit."""
+    b = W.make_batch(spec, keep_dense=True)
+    kc, vc = appended(orc, b)
+    NB, Hkv, bs, D = kc.shape
+    rng = np.random.default_rng(seed)
+    used = [(s, j) for s in range(b.num_dec) for j in range(W.cdiv(int(b.lens_dec[s]), bs))]
+    src = np.array(sorted({int(b.tables_dec[s, j]) for s, j in used}), np.int32)
+    hNB = len(src) + 5
+    dst = rng.permutation(hNB)[:len(src)].astype(np.int32)
+    fill = rng.standard_normal((hNB, Hkv, bs, D)).astype(np.float16)
+    hk, hv = orc.copy_blocks(kc, vc, fill, fill[::-1].copy(), src, dst)
+    where = dict(zip(src.tolist(), dst.tolist()))
+    tab = np.zeros_like(b.tables_dec)
+    for s, j in used:
+        tab[s, j] = where[int(b.tables_dec[s, j])]
+    got = orc.decode(b.q_dec, hk, hv, tab, b.lens_dec, b.scale)
+    ref = dense_decode_reference(b)
+    err = float(np.max(np.abs(got - ref)))
+    assert err <= 1e-12, f"{spec.name}: decode after swap-out vs dense {err:.3g}"
+    other = np.setdiff1d(np.arange(hNB), dst)
+    assert np.array_equal(hk[other].view(np.uint16), fill[other].view(np.uint16)), \
+        "blocks outside the copy changed (K)"
+    assert np.array_equal(hv[other].view(np.uint16), fill[::-1][other].view(np.uint16)), \
+        "blocks outside the copy changed (V)"
+    back = rng.permutation(NB)[:len(src)].astype(np.int32)
+    zk = np.zeros_like(kc)
+    bk, bv = orc.copy_blocks(hk, hv, zk, zk, dst, back)
+    where2 = dict(zip(dst.tolist(), back.tolist()))
+    tab2 = np.zeros_like(tab)
+    for s, j in used:
+        tab2[s, j] = where2[int(tab[s, j])]
+    got2 = orc.decode(b.q_dec, bk, bv, tab2, b.lens_dec, b.scale)
+    assert np.array_equal(got2, got), "swap-in changed the decode"
+
+
 ALL_PINS = ["half_decoding", "dense_decode", "dense_prefill", "closed_forms",
             "permutation", "sharing", "shared_prefix_diagram",
-            "page_table_diagram", "append_golden", "append_roundtrip"]
+            "page_table_diagram", "append_golden", "append_roundtrip", "swap"]
 
 
 def run_pin(orc, name):
@@ -396,6 +438,9 @@ def run_pin(orc, name):
         pin_page_table_diagram(orc)
     elif name == "append_golden":
         pin_append_golden(orc)
+    elif name == "swap":
+        for sp in small_specs()[:3]:
+            pin_swap(orc, sp)
     elif name == "append_roundtrip":
         for sp in small_specs()[:2] + [small_mixed_spec(), small_shared_spec()]:
             pin_append_roundtrip(orc, sp)

@@ -210,3 +210,99 @@ def test_build_tables_and_batch_append():
     assert bm.num_free == free and bm.seq_len(10) == 6
     with pytest.raises(pkv.PkvError):
         bm.build_tables([12], 2)                           # table wider than 2
+
+
+def test_swap_moves_a_request_between_managers():
+    # The pages' swap manager: a GPU and a CPU block manager; swap-out takes
+    # CPU blocks for the request's tokens and frees its GPU blocks, swap-in
+    # the reverse (§4.4).
+    gpu, cpu = pkv.BlockManager(8, 16), pkv.BlockManager(6, 16)
+    gpu.allocate(1, 40)                     # blocks 7, 6, 5
+    gpu.allocate(2, 16)                     # block 4
+    src, dst = gpu.swap_to(cpu, 1)
+    assert list(src) == [7, 6, 5] and list(dst) == [5, 4, 3]
+    assert gpu.seq_len(1) == -1 and cpu.seq_len(1) == 40
+    assert gpu.num_free == 7 and cpu.num_free == 3
+    gpu.allocate(3, 48)                     # reuses the freed blocks 5, 6, 7
+    assert list(gpu.block_table(3)) == [5, 6, 7]
+    src, dst = cpu.swap_to(gpu, 1)          # back into whatever is free
+    assert list(src) == [5, 4, 3] and list(dst) == [3, 2, 1]
+    assert gpu.seq_len(1) == 40 and list(gpu.block_table(1)) == [3, 2, 1]
+    assert cpu.num_free == 6
+
+
+def test_swap_without_room_changes_nothing():
+    gpu, cpu = pkv.BlockManager(8, 16), pkv.BlockManager(2, 16)
+    gpu.allocate(1, 33)                     # 3 blocks, the CPU pool holds 2
+    with pytest.raises(pkv.OutOfBlocks):
+        gpu.swap_to(cpu, 1)
+    assert gpu.seq_len(1) == 33 and list(gpu.block_table(1)) == [7, 6, 5]
+    assert cpu.num_free == 2
+    with pytest.raises(pkv.PkvError):
+        gpu.swap_to(pkv.BlockManager(8, 32), 1)   # block sizes differ
+    with pytest.raises(pkv.PkvError):
+        gpu.swap_to(cpu, 99)                       # unknown request
+
+
+def test_swap_of_a_forked_request_keeps_the_shared_prefix():
+    gpu, cpu = pkv.BlockManager(8, 16), pkv.BlockManager(8, 16)
+    gpu.allocate(1, 32)                     # blocks 7, 6
+    gpu.fork(1, 2, 32)                      # request 2 shares both
+    gpu.append_token(2)                     # and owns block 5
+    src, dst = gpu.swap_to(cpu, 2)
+    assert list(src) == [7, 6, 5]           # all three are copied
+    assert list(gpu.block_table(1)) == [7, 6]
+    assert gpu.num_free == 6                # only the private block came back
+    src, dst = cpu.swap_to(gpu, 2)          # swapped in as private blocks
+    assert len(set(gpu.block_table(2)) & set(gpu.block_table(1))) == 0
+
+
+def test_random_swaps_match_the_pages_model():
+    rng = np.random.default_rng(23)
+    bs = 16
+    gpu, cpu = pkv.BlockManager(48, bs), pkv.BlockManager(24, bs)
+    mg, mc = PagesModel(48, bs), PagesModel(24, bs)
+    where = {}                                # request -> "g" or "c"
+    nxt = 0
+    for _ in range(2000):
+        op = rng.integers(0, 6)
+        on_gpu = [r for r, w in where.items() if w == "g"]
+        on_cpu = [r for r, w in where.items() if w == "c"]
+        if op == 0 or not where:
+            n = int(rng.integers(1, 60))
+            if mg.allocate(nxt, n):
+                gpu.allocate(nxt, n)
+                where[nxt] = "g"
+            else:
+                with pytest.raises(pkv.OutOfBlocks):
+                    gpu.allocate(nxt, n)
+            nxt += 1
+        elif op == 1 and on_gpu:
+            r = on_gpu[int(rng.integers(0, len(on_gpu)))]
+            want = mg.append_token(r)
+            if want is None:
+                with pytest.raises(pkv.OutOfBlocks):
+                    gpu.append_token(r)
+            else:
+                assert gpu.append_token(r) == want
+        elif op in (2, 3) and (on_gpu if op == 2 else on_cpu):
+            pool = on_gpu if op == 2 else on_cpu
+            r = pool[int(rng.integers(0, len(pool)))]
+            fm, tm = (mg, mc) if op == 2 else (mc, mg)
+            fb, tb = (gpu, cpu) if op == 2 else (cpu, gpu)
+            if len(tm.free_blocks) < len(fm.tables[r]):
+                with pytest.raises(pkv.OutOfBlocks):
+                    fb.swap_to(tb, r)
+                continue
+            held, length = list(fm.tables[r]), fm.lens[r]
+            fm.free(r)
+            assert tm.allocate(r, length)
+            src, dst = fb.swap_to(tb, r)
+            assert list(src) == held and list(dst) == tm.tables[r]
+            where[r] = "c" if op == 2 else "g"
+        elif op == 4:
+            r = list(where)[int(rng.integers(0, len(where)))]
+            (mg if where[r] == "g" else mc).free(r)
+            (gpu if where[r] == "g" else cpu).free(r)
+            del where[r]
+        assert gpu.num_free == len(mg.free_blocks) and cpu.num_free == len(mc.free_blocks)

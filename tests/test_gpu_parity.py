@@ -12,6 +12,7 @@ import pytest
 import torch
 
 import oracle
+import paged_kv_cache_407_amd as pkv
 import pins
 import workloads as W
 from gpu_util import DevBatch, max_abs, say, to_dev, to_host
@@ -462,7 +463,6 @@ def test_block_manager_drives_append_and_decode():
     kernels: prompts are written through their slots, one decode step appends
     a token per sequence (some crossing a block boundary), and the decode
     reads the new tokens back through the manager's tables."""
-    import paged_kv_cache_407_amd as pkv
     rng = np.random.default_rng(99)
     Hq, Hkv, D, bs, NB = 8, 2, 128, 16, 256
     lens = [1, 15, 16, 17, 100, 257, 33]
@@ -499,3 +499,152 @@ def test_block_manager_drives_append_and_decode():
     err = max_abs(out, ref)
     say(f"block manager end to end: max-abs {err:.3g}")
     assert err <= TIGHT_DECODE
+
+
+# -------------------------------------------------- block copies (swapping)
+def _pinned_pool(shape, fill):
+    t = torch.empty(shape, dtype=torch.float16, pin_memory=True)
+    t.copy_(torch.from_numpy(np.ascontiguousarray(fill).view(np.int16)).view(torch.float16))
+    return t
+
+
+def _pinned_ids(a):
+    t = torch.empty(len(a), dtype=torch.int32, pin_memory=True)
+    t.copy_(torch.from_numpy(np.asarray(a, np.int32)))
+    return t
+
+
+@pytest.mark.parametrize("ids_on", ["device", "pinned"])
+def test_copy_blocks_out_and_back_bit_exact(ids_on):
+    """Device pool -> pinned host pool -> fresh device pool, against the
+    oracle's block copy; the request's decode survives the round trip bit
+    for bit (the same kernel on the same bytes at other block ids)."""
+    spec = gpu_spec("swap_d128_bs16", 8, 2, 128, 16, (1, 16, 17, 200, 333), seed=31)
+    b = W.make_batch(spec)
+    dev = DevBatch(b)
+    dev.append()
+    before = to_host(dev.decode())
+    kc, vc = check_append(b, dev)
+    NB, Hkv, bs, D = kc.shape
+    rng = np.random.default_rng(7)
+    used = [(s, j) for s in range(b.num_dec) for j in range(W.cdiv(int(b.lens_dec[s]), bs))]
+    src = np.array([int(b.tables_dec[s, j]) for s, j in used], np.int32)
+    hNB = len(src) + 6
+    dst = rng.permutation(hNB)[:len(src)].astype(np.int32)
+    fill = rng.standard_normal((hNB, Hkv, bs, D)).astype(np.float16)
+    hk, hv = _pinned_pool(fill.shape, fill), _pinned_pool(fill.shape, fill[::-1])
+    mk = to_dev if ids_on == "device" else _pinned_ids
+    say("copy blocks out", len(src), "blocks, ids on", ids_on)
+    pkv.copy_blocks(dev.k_cache, dev.v_cache, hk, hv, mk(src), mk(dst))
+    torch.cuda.synchronize()
+    ok, ov = oracle.copy_blocks(kc, vc, fill, fill[::-1], src, dst)
+    assert np.array_equal(hk.numpy().view(np.uint16), ok.view(np.uint16))
+    assert np.array_equal(hv.numpy().view(np.uint16), ov.view(np.uint16))
+    back = rng.permutation(NB)[:len(src)].astype(np.int32)
+    nk = torch.zeros_like(dev.k_cache)
+    nv = torch.zeros_like(dev.v_cache)
+    say("copy blocks back")
+    pkv.copy_blocks(hk, hv, nk, nv, mk(dst), mk(back))
+    torch.cuda.synchronize()
+    bk, bv = oracle.copy_blocks(ok, ov, np.zeros_like(kc), np.zeros_like(vc), dst, back)
+    assert np.array_equal(to_host(nk).view(np.uint16), bk.view(np.uint16))
+    assert np.array_equal(to_host(nv).view(np.uint16), bv.view(np.uint16))
+    tab = b.tables_dec.copy()
+    for (s, j), p in zip(used, back):
+        tab[s, j] = p
+    after = to_host(dev.decode(tables=to_dev(tab), k_cache=nk, v_cache=nv))
+    assert np.array_equal(after.view(np.uint32), before.view(np.uint32))
+
+
+def test_copy_blocks_dma_matches_kernel():
+    """The DMA path (host id lists, one copy per run of consecutive blocks)
+    writes the same bytes as the kernel path, device -> device and device
+    -> pinned host."""
+    rng = np.random.default_rng(8)
+    NB, Hkv, bs, D = 64, 4, 16, 64
+    pool = rng.standard_normal((2, NB, Hkv, bs, D)).astype(np.float16)
+    sk, sv = to_dev(pool[0]), to_dev(pool[1])
+    src = np.array([3, 4, 5, 9, 10, 40, 41, 42, 43, 7], np.int32)   # runs of 3, 2, 4, 1
+    dst = np.array([20, 21, 22, 0, 1, 50, 51, 52, 53, 63], np.int32)
+    for kind in ("device", "pinned"):
+        if kind == "device":
+            a = [torch.zeros_like(sk) for _ in range(4)]
+        else:
+            a = [_pinned_pool(pool[0].shape, np.zeros_like(pool[0])) for _ in range(4)]
+        say("copy blocks dma vs kernel,", kind, "destination")
+        pkv.copy_blocks(sk, sv, a[0], a[1], to_dev(src), to_dev(dst))
+        pkv.copy_blocks_dma(sk, sv, a[2], a[3], src, dst)
+        torch.cuda.synchronize()
+        ref_k, ref_v = oracle.copy_blocks(pool[0], pool[1], np.zeros_like(pool[0]),
+                                          np.zeros_like(pool[1]), src, dst)
+        for t, r in ((a[0], ref_k), (a[1], ref_v), (a[2], ref_k), (a[3], ref_v)):
+            got = to_host(t) if kind == "device" else t.numpy()
+            assert np.array_equal(got.view(np.uint16), r.view(np.uint16))
+
+
+def test_copy_blocks_skips_ids_outside_pools():
+    rng = np.random.default_rng(9)
+    NB, Hkv, bs, D = 16, 2, 16, 128
+    pool = rng.standard_normal((2, NB, Hkv, bs, D)).astype(np.float16)
+    sk, sv = to_dev(pool[0]), to_dev(pool[1])
+    dk, dv = torch.zeros_like(sk), torch.zeros_like(sv)
+    src = np.array([1, -1, 2, 99, 3], np.int32)
+    dst = np.array([4, 5, 16, 6, 7], np.int32)
+    say("copy blocks with ids outside the pools")
+    pkv.copy_blocks(sk, sv, dk, dv, to_dev(src), to_dev(dst))
+    torch.cuda.synchronize()
+    ok = (src >= 0) & (src < NB) & (dst >= 0) & (dst < NB)
+    rk, rv = oracle.copy_blocks(pool[0], pool[1], np.zeros_like(pool[0]), np.zeros_like(pool[1]),
+                                src[ok], dst[ok])
+    assert np.array_equal(to_host(dk).view(np.uint16), rk.view(np.uint16))
+    assert np.array_equal(to_host(dv).view(np.uint16), rv.view(np.uint16))
+    with pytest.raises(pkv.PkvError):
+        pkv.copy_blocks_dma(sk, sv, dk, dv, src, dst)   # host-checked: rejected
+
+
+def test_swap_preempted_request_and_resume():
+    """The pages' swap flow end to end: a request is swapped out to a pinned
+    host pool (block pairs from the block managers), its GPU blocks are
+    reused and overwritten by another request, it is swapped back into other
+    GPU blocks, and its decode equals the decode before the swap."""
+    rng = np.random.default_rng(41)
+    Hq, Hkv, D, bs, NB, HNB = 8, 2, 128, 16, 24, 16
+    gpu, cpu = pkv.BlockManager(NB - 1, bs), pkv.BlockManager(HNB, bs)
+    kc = np.full((NB, Hkv, bs, D), np.nan, np.float16)
+    dk, dv = to_dev(kc), to_dev(kc)
+    L = 150
+    gpu.allocate(0, L)
+    k0 = rng.standard_normal((L, Hkv, D)).astype(np.float16)
+    v0 = rng.standard_normal((L, Hkv, D)).astype(np.float16)
+    pkv.kv_append(to_dev(k0), to_dev(v0), dk, dv, to_dev(gpu.slots(0, 0, L)))
+    q = to_dev(rng.standard_normal((1, Hq, D)).astype(np.float16))
+    scale = float(np.float32(1 / np.sqrt(D)))
+
+    def decode(r):
+        tab, lens = gpu.build_tables([r], 16, pad_block=NB - 1)
+        return to_host(pkv.paged_attention_decode(q, dk, dv, to_dev(tab), to_dev(lens),
+                                                  max_seq_len=int(lens[0]), scale=scale))
+    before = decode(0)
+    hk = _pinned_pool((HNB, Hkv, bs, D), np.zeros((HNB, Hkv, bs, D), np.float16))
+    hv = _pinned_pool((HNB, Hkv, bs, D), np.zeros((HNB, Hkv, bs, D), np.float16))
+    say("swap out request 0")
+    src, dst = gpu.swap_to(cpu, 0)
+    pkv.copy_blocks(dk, dv, hk, hv, to_dev(src), to_dev(dst))
+    gpu.allocate(1, 200)                       # takes the freed blocks and more
+    assert set(src) <= set(gpu.block_table(1))
+    junk = rng.standard_normal((200, Hkv, D)).astype(np.float16)
+    pkv.kv_append(to_dev(junk), to_dev(junk), dk, dv, to_dev(gpu.slots(1, 0, 200)))
+    gpu.free(1)
+    say("swap in request 0")
+    src2, dst2 = cpu.swap_to(gpu, 0)
+    pkv.copy_blocks(hk, hv, dk, dv, to_dev(src2), to_dev(dst2))
+    assert list(gpu.block_table(0)) != list(src)
+    after = decode(0)
+    assert np.array_equal(after.view(np.uint32), before.view(np.uint32))
+    # and the decode itself against the oracle over the request's own rows
+    tab = np.arange(W.cdiv(L, bs), dtype=np.int32)[None]
+    pk = np.zeros((tab.shape[1], Hkv, bs, D), np.float16)
+    pv = np.zeros_like(pk)
+    okc, ovc = oracle.kv_append(k0, v0, pk, pv, np.arange(L, dtype=np.int32))
+    ref = oracle.decode(to_host(q), okc, ovc, tab, np.array([L], np.int32), scale)
+    assert max_abs(after, ref) <= TIGHT_DECODE

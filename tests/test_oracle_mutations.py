@@ -37,6 +37,13 @@ MUTATIONS = [
     ("chunk prefix", "int32_t prefix = seq_lens[c] - (cu_q_lens[c + 1] - cu_q_lens[c]);",
      "int32_t prefix = seq_lens[c] - (cu_q_lens[c + 1] - cu_q_lens[c]) - 1;"),
     ("last token dropped", "seq_lens[s], h / group,", "seq_lens[s] - (seq_lens[s] > 1), h / group,"),
+    ("copy layout", "int64_t to = ((d * num_kv_heads + h) * block_size + o) * head_dim + e;",
+     "int64_t to = ((d * block_size + o) * num_kv_heads + h) * head_dim + e;"),
+    ("copy V from K", "dst_v[to] = src_v[from];", "dst_v[to] = src_k[from];"),
+    ("copy wrong pair", "int64_t s = src_blocks[i], d = dst_blocks[i];",
+     "int64_t s = src_blocks[(i + 1) % count], d = dst_blocks[i];"),
+    ("copy offset", "int64_t from = ((s * num_kv_heads + h) * block_size + o) * head_dim + e;",
+     "int64_t from = ((s * num_kv_heads + h) * block_size + (block_size - 1 - o)) * head_dim + e;"),
 ]
 
 
