@@ -72,6 +72,12 @@ def parse():
                          "host pool and back (kernel and DMA paths); one JSON line per "
                          "direction and path")
     ap.add_argument("--swap-blocks", type=int, default=1024)
+    ap.add_argument("--serve", action="store_true",
+                    help="multi-step continuous batching: the native scheduler drives "
+                         "append / prefill / decode over many steps; prints one JSON line")
+    ap.add_argument("--serve-requests", type=int, default=256)
+    ap.add_argument("--serve-batch", type=int, default=32)
+    ap.add_argument("--serve-tokens", type=int, default=2048)
     ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH",
                                                           "COPY_WRITE"),
                     help="turn four rocprofv3 --pmc output folders (FETCH_SIZE and "
@@ -217,6 +223,9 @@ def main():
         return
     if args.swap_bench:
         swap_bench(args, dev)
+        return
+    if args.serve:
+        serve_bench(args, dev)
         return
 
     t0 = time.time()
@@ -545,6 +554,90 @@ def swap_bench(args, dev):
                           "path": path, "workload": args.workload, "blocks": n,
                           "bytes": nbytes, "us_mean": round(float(d.mean()), 1),
                           "GBps": round(gbs, 2), "calls": reps}), flush=True)
+
+
+def serve_bench(args, dev):
+    """Sustained multi-step continuous batching at the workload's attention
+    shape: every request is queued at the start (prompt ~ U[64, 1024] tokens
+    as in the pages' batch-32 comparison, generation ~ U[16, 256] tokens),
+    and the native scheduler's plans drive kv_append, the prefill chunks and
+    the decode rows until all have finished.  Query/key/value rows come from
+    a resident random buffer (their values do not change the work).  Reports
+    sequence-steps per second (prefill rows + decode rows per second of wall
+    time, host scheduling included), tokens per second, and the share of the
+    wall time the host spends planning (scheduler, staging buffer wait,
+    plan copy enqueue)."""
+    import torch
+    import paged_kv_cache_407_amd as pkv
+    from paged_kv_cache_407_amd.driver import StepDriver
+    spec = W.SPECS[args.workload]
+    NB, Hq, Hkv, D, bs = (spec.num_blocks, spec.num_q_heads, spec.num_kv_heads,
+                          spec.head_dim, spec.block_size)
+    B, T, max_len = args.serve_batch, args.serve_tokens, 1024 + 256
+    rng = np.random.default_rng(11)
+    n = args.serve_requests
+    prompts = rng.integers(64, 1025, size=n)
+    gens = rng.integers(16, 257, size=n)
+    kc = torch.randn((NB, Hkv, bs, D), device=dev).half()
+    vc = torch.randn((NB, Hkv, bs, D), device=dev).half()
+    rows = T + B
+    rk = torch.randn((rows, Hkv, D), device=dev).half()
+    rv = torch.randn((rows, Hkv, D), device=dev).half()
+    rq = torch.randn((rows, Hq, D), device=dev).half()
+    scale = float(np.float32(1 / math.sqrt(D)))
+
+    def rows_fn(plan):
+        nt = plan["num_new_tokens"]
+        return rk[:nt], rv[:nt], rq[:nt]
+
+    def run(count, record):
+        bm = pkv.BlockManager(NB - 1, bs)
+        sch = pkv.Scheduler(bm, B, T, max_len)
+        for i in range(count):
+            sch.add_request(i, int(prompts[i]), int(gens[i]))
+        drv = StepDriver(sch, kc, vc, Hq, scale, rows_fn, pad_block=NB - 1)
+        st = dict(steps=0, rows=0, prefill_rows=0, decode_rows=0, prefill_tokens=0,
+                  finished=0, preempted=0, host_s=0.0)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while st["finished"] < count:
+            h0 = time.perf_counter()
+            plan, _, _ = drv.step()
+            st["host_s"] += time.perf_counter() - h0
+            st["steps"] += 1
+            st["prefill_rows"] += len(plan["prefill_ids"])
+            st["decode_rows"] += len(plan["decode_ids"])
+            st["prefill_tokens"] += int(plan["cu_q_lens"][-1])
+            st["finished"] += len(plan["finished"])
+            st["preempted"] += len(plan["preempted"])
+        torch.cuda.synchronize()
+        st["wall_s"] = time.perf_counter() - t0
+        st["plan_s"] = drv.plan_s
+        drv.close()
+        return st
+
+    run(min(n, 2 * B), False)                         # warm-up (kernels, allocator)
+    st = run(n, True)
+    seq_steps = st["prefill_rows"] + st["decode_rows"]
+    log(f"serve: {n} requests, {st['steps']} steps, {st['wall_s'] * 1e3:.1f} ms, "
+        f"{seq_steps / st['wall_s']:.0f} seq-steps/s, {st['decode_rows'] / st['wall_s']:.0f} "
+        f"decode tokens/s, {st['preempted']} preempted")
+    print(json.dumps({
+        "metric": "seq-steps/s (multi-step continuous batching)", "workload": args.workload,
+        "value": round(seq_steps / st["wall_s"], 1), "unit": "seq-steps/s",
+        "requests": n, "max_batch_size": B, "max_num_tokens": T, "steps": st["steps"],
+        "wall_ms": round(st["wall_s"] * 1e3, 2),
+        "ms_per_step": round(st["wall_s"] * 1e3 / st["steps"], 4),
+        "decode_tokens_per_s": round(st["decode_rows"] / st["wall_s"], 1),
+        "prefill_tokens_per_s": round(st["prefill_tokens"] / st["wall_s"], 1),
+        "requests_per_s": round(n / st["wall_s"], 2),
+        "host_share": round(st["host_s"] / st["wall_s"], 3),
+        "plan_share": round(st["plan_s"] / st["wall_s"], 4),
+        "preempted": st["preempted"], "prompt_tokens": int(prompts.sum()),
+        "generated_tokens": int(gens.sum()),
+        "config": {"num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D, "block_size": bs,
+                   "num_blocks": NB, "prompt": "U[64,1024]", "generate": "U[16,256]"}}),
+        flush=True)
 
 
 def cpu_baseline(b: W.Batch, kv_bytes: int, budget_s: float) -> dict:

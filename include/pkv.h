@@ -180,6 +180,8 @@ pkv_block_manager *pkv_bm_create(int32_t num_blocks, int32_t block_size);
 void pkv_bm_destroy(pkv_block_manager *bm);
 /* Free blocks, or -1 for a NULL manager. */
 int32_t pkv_bm_num_free(const pkv_block_manager *bm);
+/* The block size the manager was created with; -1 for NULL. */
+int32_t pkv_bm_block_size(const pkv_block_manager *bm);
 /* A new request holding num_tokens tokens (e.g. a prompt to prefill).
  * PKV_ERR_INVALID if the id exists; PKV_ERR_NO_BLOCKS (nothing taken) if
  * fewer than ceil(num_tokens / block_size) blocks are free. */
@@ -228,6 +230,99 @@ int pkv_bm_slots(const pkv_block_manager *bm, int64_t request_id,
 int pkv_bm_swap(pkv_block_manager *from, pkv_block_manager *to, int64_t request_id,
                 int32_t *src_blocks, int32_t *dst_blocks, int32_t capacity,
                 int32_t *count);
+
+/*
+ * Iteration-level scheduler (continuous batching) over a block manager
+ * ("LLM 推理引擎 …", §2.2 ContinuousBatchingScheduler, §4.3 Chunked
+ * Prefill, §5.4 Preemption; plain host code, not thread-safe).  Each call of
+ * pkv_sched_step closes the previous step (its prefill chunks and decode
+ * tokens count as written) and plans the next one:
+ *   1. requests that have written their prompt and run max_new_tokens
+ *      decode steps finish and free their blocks;
+ *   2. waiting requests are admitted in arrival order while fewer than
+ *      max_batch_size run and ceil(prompt / block_size) blocks can be taken
+ *      (the first that does not fit stays at the head);
+ *   3. while the decode rows of the step need more new blocks than are
+ *      free, the most recently admitted running request is preempted: its
+ *      blocks are freed, it goes back to the head of the waiting queue and
+ *      its generated tokens join its prompt (recomputed on readmission);
+ *   4. the batch: prompt chunks of the running requests still prefilling,
+ *      in admission order, within max_num_tokens new tokens (a prompt that
+ *      does not fit the rest of the budget is cut, its remainder comes next
+ *      step), then one decode row per request that has written its prompt,
+ *      while the batch has fewer than max_batch_size rows.
+ * The plan's arrays are the kernels' inputs: cu_q_lens / prefill_tables /
+ * prefill_lens (seq_len = the prompt tokens written so far plus this chunk)
+ * for pkv_paged_attention_prefill; decode_tables / decode_lens for
+ * pkv_paged_attention_decode; slot_mapping (the chunks' positions in
+ * cu_q_lens order, then one new slot per decode row) for pkv_kv_append.
+ * Capacities the caller provides: max_batch_size rows (ids, lens,
+ * cu_q_lens + 1), max_batch_size * max_blocks_per_seq table entries,
+ * max_num_tokens + max_batch_size slots, max_batch_size finished and
+ * preempted ids (those two may be NULL).  max_blocks_per_seq * block_size
+ * must cover max_seq_len, and a request's prompt plus max_new_tokens must
+ * not exceed max_seq_len (checked when it is added).
+ */
+typedef struct pkv_scheduler pkv_scheduler;
+typedef struct {
+  int32_t num_prefill;        /* prefill rows (chunks) */
+  int32_t num_prefill_tokens; /* their new tokens = cu_q_lens[num_prefill] */
+  int32_t num_decode;         /* decode rows */
+  int32_t num_new_tokens;     /* slot_mapping entries */
+  int32_t num_finished;       /* requests that finished at this boundary */
+  int32_t num_preempted;      /* requests preempted by this step */
+} pkv_step_plan;
+pkv_scheduler *pkv_sched_create(pkv_block_manager *bm, int32_t max_batch_size,
+                                int32_t max_num_tokens, int32_t max_seq_len);
+void pkv_sched_destroy(pkv_scheduler *s);
+int pkv_sched_add_request(pkv_scheduler *s, int64_t request_id, int32_t prompt_len,
+                          int32_t max_new_tokens);
+int32_t pkv_sched_num_waiting(const pkv_scheduler *s);
+int32_t pkv_sched_num_running(const pkv_scheduler *s);
+int pkv_sched_step(pkv_scheduler *s, int32_t max_blocks_per_seq, int32_t pad_block,
+                   pkv_step_plan *plan, int64_t *prefill_ids, int32_t *cu_q_lens,
+                   int32_t *prefill_tables, int32_t *prefill_lens, int64_t *decode_ids,
+                   int32_t *decode_tables, int32_t *decode_lens, int32_t *slot_mapping,
+                   int64_t *finished_ids, int64_t *preempted_ids);
+
+/*
+ * Native step executor over a scheduler (continuous batching, "LLM 推理引擎
+ * …", §2.2: each forward step runs the recomposed batch, prefill chunks and
+ * decode rows together).  pkv_server_create allocates, once: two pinned
+ * staging buffers and two device copies of a step's plan, and the decode
+ * workspace for max_batch_size rows of up to max_seq_len tokens.  max_batch_size,
+ * max_num_tokens and max_seq_len must equal the scheduler's; the pools are
+ * the caller's device buffers ([num_blocks][Hkv][bs][D] fp16, bs = the
+ * block manager's).  NULL on invalid arguments or a failed allocation.
+ *   pkv_server_plan: runs pkv_sched_step into the staging buffer not used
+ *     by the previous step (after waiting for its copy of two steps ago)
+ *     and enqueues its host-to-device copy on `stream`.
+ *   pkv_server_plan_arrays: host views of the last plan's request ids,
+ *     cu_q_lens, prefill_lens, decode_lens, finished and preempted ids
+ *     (valid until the next plan), for the caller to produce the step's rows.
+ *   pkv_server_execute: enqueues on `stream` the kv append of the plan's
+ *     new rows, then the prefill of its chunks and the decode of its decode
+ *     rows.  new_k / new_v [num_new_tokens][Hkv][D] and q
+ *     [num_new_tokens][Hq][D] fp16, device, in slot_mapping order (the
+ *     chunks' tokens, then one row per decode request); out_prefill
+ *     [num_prefill_tokens][Hq][D] and out_decode [num_decode][Hq][D] fp32,
+ *     device (may be NULL when the step has no such rows).
+ * Use one stream for all calls of a server.
+ */
+typedef struct pkv_server pkv_server;
+pkv_server *pkv_server_create(pkv_scheduler *sched, pkv_block_manager *bm, void *k_cache,
+                              void *v_cache, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t num_blocks, int32_t pad_block,
+                              int32_t max_batch_size, int32_t max_num_tokens,
+                              int32_t max_seq_len, float scale);
+void pkv_server_destroy(pkv_server *s);
+int pkv_server_plan(pkv_server *s, pkv_step_plan *plan, void *stream);
+int pkv_server_plan_arrays(const pkv_server *s, const int64_t **prefill_ids,
+                           const int32_t **cu_q_lens, const int32_t **prefill_lens,
+                           const int64_t **decode_ids, const int32_t **decode_lens,
+                           const int64_t **finished_ids, const int64_t **preempted_ids);
+int pkv_server_execute(pkv_server *s, const void *new_k, const void *new_v, const void *q,
+                       float *out_prefill, float *out_decode, void *stream);
 
 /*
  * Block copies between two KV pools ("LLM 推理引擎 …", §4.4 Swap: the

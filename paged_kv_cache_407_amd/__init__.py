@@ -49,6 +49,20 @@ SIGNATURES = {
     "pkv_bm_build_tables": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _P, _P]),
     "pkv_bm_slots": (ctypes.c_int, [_P, _I64, _I32, _I32, _P]),
     "pkv_bm_swap": (ctypes.c_int, [_P, _P, _I64, _P, _P, _I32, _P]),
+    "pkv_bm_block_size": (_I32, [_P]),
+    "pkv_sched_create": (_P, [_P, _I32, _I32, _I32]),
+    "pkv_sched_destroy": (None, [_P]),
+    "pkv_sched_add_request": (ctypes.c_int, [_P, _I64, _I32, _I32]),
+    "pkv_sched_num_waiting": (_I32, [_P]),
+    "pkv_sched_num_running": (_I32, [_P]),
+    "pkv_sched_step": (ctypes.c_int, [_P, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                      _P]),
+    "pkv_server_create": (_P, [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                               _F]),
+    "pkv_server_destroy": (None, [_P]),
+    "pkv_server_plan": (ctypes.c_int, [_P, _P, _P]),
+    "pkv_server_plan_arrays": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P]),
+    "pkv_server_execute": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P]),
     "pkv_copy_blocks": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
                                        _I32, _P]),
     "pkv_copy_blocks_dma": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32,
@@ -369,3 +383,89 @@ class BlockManager:
         self._rc(self._lib.pkv_bm_swap(self._h, other._h, int(request_id), src.ctypes.data,
                                        dst.ctypes.data, n, ctypes.byref(cnt)), "swap")
         return src[:cnt.value], dst[:cnt.value]
+
+
+class _StepPlan(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("num_prefill", "num_prefill_tokens",
+                                              "num_decode", "num_new_tokens",
+                                              "num_finished", "num_preempted")]
+
+
+class StepPlan:
+    """One step of the scheduler: numpy arrays sized to what the step uses.
+    prefill_*: chunk rows (cu_q_lens has num_prefill + 1 entries); decode_*:
+    decode rows; slot_mapping: the chunks' slots in cu_q_lens order, then one
+    per decode row."""
+
+    def __init__(self, **kw):
+        self.__dict__.update(kw)
+
+
+class Scheduler:
+    """Iteration-level scheduler of libpkv (``pkv_sched_*``) over a
+    ``BlockManager``: admission, chunked prefill within a token budget,
+    decode rows, preemption by recompute; ``step()`` closes the previous
+    step and plans the next one."""
+
+    def __init__(self, block_manager: BlockManager, max_batch_size: int, max_num_tokens: int,
+                 max_seq_len: int):
+        import numpy as np
+        self._np = np
+        self._lib = load_library()
+        self.bm = block_manager
+        self._h = self._lib.pkv_sched_create(block_manager._h, int(max_batch_size),
+                                             int(max_num_tokens), int(max_seq_len))
+        if not self._h:
+            raise PkvError("pkv_sched_create: invalid arguments")
+        self.max_batch_size, self.max_num_tokens = int(max_batch_size), int(max_num_tokens)
+        self.max_seq_len = int(max_seq_len)
+
+    def close(self):
+        if self._h:
+            self._lib.pkv_sched_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def add_request(self, request_id: int, prompt_len: int, max_new_tokens: int):
+        _check(self._lib.pkv_sched_add_request(self._h, int(request_id), int(prompt_len),
+                                               int(max_new_tokens)), "add_request")
+
+    @property
+    def num_waiting(self) -> int:
+        return int(self._lib.pkv_sched_num_waiting(self._h))
+
+    @property
+    def num_running(self) -> int:
+        return int(self._lib.pkv_sched_num_running(self._h))
+
+    def step(self, max_blocks_per_seq: int, pad_block: int = 0) -> StepPlan:
+        np = self._np
+        B, T, MB = self.max_batch_size, self.max_num_tokens, int(max_blocks_per_seq)
+        a = dict(prefill_ids=np.empty(B, np.int64), cu_q_lens=np.empty(B + 1, np.int32),
+                 prefill_tables=np.empty((B, MB), np.int32), prefill_lens=np.empty(B, np.int32),
+                 decode_ids=np.empty(B, np.int64), decode_tables=np.empty((B, MB), np.int32),
+                 decode_lens=np.empty(B, np.int32), slot_mapping=np.empty(T + B, np.int32),
+                 finished=np.empty(B, np.int64), preempted=np.empty(B, np.int64))
+        plan = _StepPlan()
+        rc = self._lib.pkv_sched_step(
+            self._h, MB, int(pad_block), ctypes.byref(plan), a["prefill_ids"].ctypes.data,
+            a["cu_q_lens"].ctypes.data, a["prefill_tables"].ctypes.data,
+            a["prefill_lens"].ctypes.data, a["decode_ids"].ctypes.data,
+            a["decode_tables"].ctypes.data, a["decode_lens"].ctypes.data,
+            a["slot_mapping"].ctypes.data, a["finished"].ctypes.data,
+            a["preempted"].ctypes.data)
+        _check(rc, "sched_step")
+        P, D = plan.num_prefill, plan.num_decode
+        return StepPlan(
+            prefill_ids=a["prefill_ids"][:P], cu_q_lens=a["cu_q_lens"][:P + 1],
+            prefill_tables=a["prefill_tables"][:P], prefill_lens=a["prefill_lens"][:P],
+            decode_ids=a["decode_ids"][:D], decode_tables=a["decode_tables"][:D],
+            decode_lens=a["decode_lens"][:D], slot_mapping=a["slot_mapping"][:plan.num_new_tokens],
+            finished=a["finished"][:plan.num_finished],
+            preempted=a["preempted"][:plan.num_preempted],
+            num_prefill_tokens=plan.num_prefill_tokens)

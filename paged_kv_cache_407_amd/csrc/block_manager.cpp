@@ -73,6 +73,10 @@ int32_t pkv_bm_num_free(const pkv_block_manager *bm) {
   return bm ? (int32_t)bm->free_list.size() : -1;
 }
 
+int32_t pkv_bm_block_size(const pkv_block_manager *bm) {
+  return bm ? bm->block_size : -1;
+}
+
 int pkv_bm_allocate(pkv_block_manager *bm, int64_t request_id,
                     int32_t num_tokens) {
   if (!bm || num_tokens < 0 || bm->find(request_id)) return PKV_ERR_INVALID;
