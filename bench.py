@@ -243,6 +243,9 @@ def main():
     pf_flops = W.prefill_flops(b)
     max_len = int(b.lens_dec.max()) if S else 1
     max_q = int(np.diff(b.cu_q_lens).max()) if C else 0
+    max_len_pf = int(b.lens_pf.max()) if C else 1
+    pf_ws_bytes = (pkv.prefill_workspace_size(C, int(b.cu_q_lens[-1]), max_q, spec.num_q_heads,
+                                              spec.head_dim, max_len_pf) if C else 0)
     part = pkv.decode_partition_size(S, spec.num_q_heads, spec.num_kv_heads, spec.head_dim,
                                      spec.block_size, max_len, args.partition_size)
     ws_bytes = pkv.decode_workspace_size(S, spec.num_q_heads, spec.num_kv_heads,
@@ -283,6 +286,8 @@ def main():
         tab, lens = to_dev(b.tables_dec), to_dev(b.lens_dec)
     if C:
         tabp, lensp, cu = to_dev(b.tables_pf), to_dev(b.lens_pf), to_dev(b.cu_q_lens)
+        # one stream runs every step in turn: the replicas share it
+        ws_pf = torch.empty(pf_ws_bytes, dtype=torch.uint8, device=dev) if pf_ws_bytes else None
     torch.cuda.synchronize()
 
     def do_append(rep):
@@ -295,7 +300,8 @@ def main():
 
     def do_prefill(rep):
         pkv.paged_attention_prefill(rep["qp"], cu, rep["kc"], rep["vc"], tabp, lensp,
-                                    max_q_len=max_q, scale=b.scale, out=rep["outp"])
+                                    max_q_len=max_q, max_seq_len=max_len_pf, scale=b.scale,
+                                    out=rep["outp"], workspace=ws_pf)
 
     def step(rep):
         do_append(rep)

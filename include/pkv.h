@@ -148,8 +148,24 @@ int pkv_paged_attention_decode(float *out, const void *q, const void *k_cache,
  *   seq_lens     : [num_chunks] int32, device, chunk_len <= seq_len
  *   max_q_len    : host-side upper bound of the chunk lengths (rows past
  *                  it are not computed)
+ *   max_seq_len  : host-side upper bound of seq_lens, at most
+ *                  max_blocks_per_seq * block_size; a chunk whose seq_len
+ *                  exceeds it gets NaN rows
  *   scale        : as for the decode
+ *   workspace    : device scratch of at least pkv_prefill_workspace_size()
+ *                  bytes, 256-byte aligned (may be NULL when that size is 0).
+ *                  When the grid of query tiles is small, a query tile's key
+ *                  range is cut into parts run by different workgroups; the
+ *                  parts leave partial outputs here and a second kernel
+ *                  combines them.  Contents on entry do not matter; calls
+ *                  sharing one workspace must be ordered (same stream).
+ * Errors: PKV_ERR_INVALID for bad sizes, misaligned pointers or a missing
+ * or short workspace; PKV_ERR_UNSUPPORTED for head_dim / block_size without
+ * an instance.
  */
+size_t pkv_prefill_workspace_size(int32_t num_chunks, int32_t total_q_tokens,
+                                  int32_t max_q_len, int32_t num_q_heads,
+                                  int32_t head_dim, int32_t max_seq_len);
 int pkv_paged_attention_prefill(float *out, const void *q,
                                 const int32_t *cu_q_lens, const void *k_cache,
                                 const void *v_cache,
@@ -159,7 +175,8 @@ int pkv_paged_attention_prefill(float *out, const void *q,
                                 int32_t num_q_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t block_size,
                                 int32_t num_blocks, int32_t max_blocks_per_seq,
-                                float scale, void *stream);
+                                int32_t max_seq_len, float scale, void *workspace,
+                                size_t workspace_bytes, void *stream);
 
 /*
  * Host-side block manager (plain host code, no device calls, not

@@ -35,7 +35,9 @@ SIGNATURES = {
     "pkv_paged_attention_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32,
                                                   _I32, _I32, _I32, _I32, _F, _I32, _P, _SZ, _P]),
     "pkv_paged_attention_prefill": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32,
-                                                   _I32, _I32, _I32, _I32, _I32, _I32, _F, _P]),
+                                                   _I32, _I32, _I32, _I32, _I32, _I32, _I32, _F,
+                                                   _P, _SZ, _P]),
+    "pkv_prefill_workspace_size": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32]),
     "pkv_bm_create": (_P, [_I32, _I32]),
     "pkv_bm_destroy": (None, [_P]),
     "pkv_bm_num_free": (_I32, [_P]),
@@ -195,9 +197,21 @@ def paged_attention_decode(q, k_cache, v_cache, block_tables, seq_lens, *, max_s
     return out
 
 
+def prefill_workspace_size(num_chunks, total_q_tokens, max_q_len, num_q_heads, head_dim,
+                           max_seq_len) -> int:
+    return int(load_library().pkv_prefill_workspace_size(num_chunks, total_q_tokens, max_q_len,
+                                                         num_q_heads, head_dim, max_seq_len))
+
+
 def paged_attention_prefill(q, cu_q_lens, k_cache, v_cache, block_tables, seq_lens, *,
-                            max_q_len: int, scale: float | None = None, out=None, stream=None):
-    """out[sum C, Hq, D] (float32) of causal chunks on paged prefixes."""
+                            max_q_len: int, max_seq_len: int | None = None,
+                            scale: float | None = None, out=None, workspace=None, stream=None):
+    """out[sum C, Hq, D] (float32) of causal chunks on paged prefixes.
+
+    ``max_seq_len`` bounds seq_lens (default: the block table's capacity).
+    ``workspace`` (uint8, at least ``prefill_workspace_size(...)`` bytes)
+    holds the partial outputs of split key ranges; without it a buffer is
+    allocated for the call."""
     NB, Hkv, bs, D = _cache_shape(k_cache, v_cache)
     _dev(q, "q", torch.float16, 3)
     _dev(cu_q_lens, "cu_q_lens", torch.int32, 1)
@@ -209,16 +223,26 @@ def paged_attention_prefill(q, cu_q_lens, k_cache, v_cache, block_tables, seq_le
         raise ValueError("q / cu_q_lens / block_tables / seq_lens shapes disagree")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
+    MB = block_tables.shape[1]
+    if max_seq_len is None:
+        max_seq_len = MB * bs
     if out is None:
         out = torch.empty((T, Hq, D), dtype=torch.float32, device=q.device)
     _dev(out, "out", torch.float32, 3)
     if out.shape != (T, Hq, D):
         raise ValueError("out shape")
+    need = prefill_workspace_size(C, T, int(max_q_len), Hq, D, int(max_seq_len))
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr, ws_bytes = 0, 0
+    if workspace is not None:
+        _dev(workspace, "workspace", torch.uint8, 1)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
     rc = load_library().pkv_paged_attention_prefill(
         out.data_ptr(), q.data_ptr(), cu_q_lens.data_ptr(), k_cache.data_ptr(),
         v_cache.data_ptr(), block_tables.data_ptr(), seq_lens.data_ptr(), C, T,
-        int(max_q_len), Hq, Hkv, D, bs, NB, block_tables.shape[1], float(scale),
-        _stream(stream))
+        int(max_q_len), Hq, Hkv, D, bs, NB, MB, int(max_seq_len), float(scale), ws_ptr,
+        ws_bytes, _stream(stream))
     _check(rc, "paged_attention_prefill")
     return out
 

@@ -81,6 +81,47 @@ WorkspaceLayout layout(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
 
 int hip_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_HIP; }
 
+// Prefill key-range split.  Query tiles are 128 rows, key tiles 64 tokens.
+// When the query tiles (x heads x chunks) are fewer than the workgroups the
+// chip holds at once -- 256 CUs x 2 workgroups of the head-dim-128 kernel --
+// part of the chip idles while each workgroup walks its whole key range.
+// The key range of a query tile is then cut into parts of at least
+// kMinSplitTiles tiles until the grid reaches about that many workgroups.
+// Larger grids are not split: the parts' partial outputs cost a write and a
+// read of fp32 rows, which a full chip does not win back.
+constexpr int kPrefillTargetWorkgroups = 512;
+constexpr int kMinSplitTiles = 4;
+
+struct PrefillSplit {
+  int32_t parts = 1, tiles = 1;
+  size_t o_off = 0, m_off = 0, l_off = 0, bytes = 0;
+};
+
+PrefillSplit prefill_split(int32_t num_chunks, int32_t total_q, int32_t max_q_len,
+                           int32_t num_q_heads, int32_t head_dim, int32_t max_seq_len) {
+  PrefillSplit s;
+  if (num_chunks <= 0 || total_q <= 0 || max_q_len <= 0 || num_q_heads <= 0 ||
+      max_seq_len <= 0)
+    return s;
+  const int64_t base = ((int64_t)max_q_len + 127) / 128 * num_chunks * num_q_heads;
+  const int64_t nt_max = ((int64_t)max_seq_len + 63) / 64;
+  int64_t parts = (kPrefillTargetWorkgroups + base - 1) / base;
+  parts = std::max<int64_t>(1, std::min<int64_t>(parts, nt_max / kMinSplitTiles));
+  s.tiles = (int32_t)((nt_max + parts - 1) / parts);
+  s.parts = (int32_t)((nt_max + s.tiles - 1) / s.tiles);
+  if (s.parts <= 1) {
+    s.parts = 1;
+    s.tiles = (int32_t)std::max<int64_t>(nt_max, 1);
+    return s;
+  }
+  const size_t rows = (size_t)s.parts * total_q * num_q_heads;
+  s.o_off = 0;
+  s.m_off = round_up((int64_t)(rows * head_dim * sizeof(float)), 256);
+  s.l_off = s.m_off + round_up((int64_t)(rows * sizeof(float)), 256);
+  s.bytes = s.l_off + round_up((int64_t)(rows * sizeof(float)), 256);
+  return s;
+}
+
 }  // namespace
 
 namespace {
@@ -230,6 +271,13 @@ int pkv_paged_attention_decode(float *out, const void *q, const void *k_cache,
   return hip_status(launch_decode(p, head_dim, block_size, (hipStream_t)stream));
 }
 
+size_t pkv_prefill_workspace_size(int32_t num_chunks, int32_t total_q_tokens,
+                                  int32_t max_q_len, int32_t num_q_heads,
+                                  int32_t head_dim, int32_t max_seq_len) {
+  return prefill_split(num_chunks, total_q_tokens, max_q_len, num_q_heads, head_dim,
+                       max_seq_len).bytes;
+}
+
 int pkv_paged_attention_prefill(float *out, const void *q,
                                 const int32_t *cu_q_lens, const void *k_cache,
                                 const void *v_cache,
@@ -239,11 +287,15 @@ int pkv_paged_attention_prefill(float *out, const void *q,
                                 int32_t num_q_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t block_size,
                                 int32_t num_blocks, int32_t max_blocks_per_seq,
-                                float scale, void *stream) {
+                                int32_t max_seq_len, float scale, void *workspace,
+                                size_t workspace_bytes, void *stream) {
   if (num_chunks < 0 || total_q_tokens < 0 || max_q_len < 0 ||
       num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
       block_size <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 ||
-      num_q_heads % num_kv_heads || !isfinite(scale) || !(scale > 0.f))
+      max_seq_len <= 0 || num_q_heads % num_kv_heads || !isfinite(scale) ||
+      !(scale > 0.f))
+    return PKV_ERR_INVALID;
+  if ((int64_t)max_seq_len > (int64_t)max_blocks_per_seq * block_size)
     return PKV_ERR_INVALID;
   if (num_q_heads > 65535 || num_chunks > 65535) return PKV_ERR_INVALID;
   if (!supported_prefill(head_dim, block_size)) return PKV_ERR_UNSUPPORTED;
@@ -269,7 +321,21 @@ int pkv_paged_attention_prefill(float *out, const void *q,
   p.group = num_q_heads / num_kv_heads;
   p.num_blocks = num_blocks;
   p.max_blocks_per_seq = max_blocks_per_seq;
+  p.max_seq_len = max_seq_len;
   p.scale_log2e = scale * kLog2e;
+  const PrefillSplit sp = prefill_split(num_chunks, total_q_tokens, max_q_len, num_q_heads,
+                                        head_dim, max_seq_len);
+  p.num_splits = sp.parts;
+  p.split_tiles = sp.tiles;
+  p.ws_o = p.ws_m = p.ws_l = nullptr;
+  if (sp.parts > 1) {
+    if (!workspace || workspace_bytes < sp.bytes || ((uintptr_t)workspace & 255u))
+      return PKV_ERR_INVALID;
+    char *w = (char *)workspace;
+    p.ws_o = (float *)(w + sp.o_off);
+    p.ws_m = (float *)(w + sp.m_off);
+    p.ws_l = (float *)(w + sp.l_off);
+  }
   return hip_status(launch_prefill(p, head_dim, block_size, max_q_len,
                                    (hipStream_t)stream));
 }

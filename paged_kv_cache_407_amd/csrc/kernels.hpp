@@ -41,8 +41,15 @@ struct PrefillParams {
   const int32_t *block_tables;  // [C][MB]
   const int32_t *seq_lens;      // [C]
   int32_t num_chunks, total_q, num_q_heads, num_kv_heads, group;
-  int32_t num_blocks, max_blocks_per_seq;
+  int32_t num_blocks, max_blocks_per_seq, max_seq_len;
   float scale_log2e;
+  // Key-range split: a query tile with n key tiles runs in
+  // min(num_splits, cdiv(n, split_tiles)) parts; with several parts each
+  // writes its unnormalised output, maximum and sum here and
+  // prefill_merge_kernel combines them.
+  float *ws_o;          // [num_splits][total_q][Hq][D]
+  float *ws_m, *ws_l;   // [num_splits][total_q][Hq]
+  int32_t num_splits, split_tiles;
 };
 
 hipError_t launch_kv_append(const AppendParams &p, hipStream_t stream);

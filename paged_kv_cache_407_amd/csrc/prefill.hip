@@ -40,6 +40,13 @@ namespace pkv {
 // log2 of the largest softmax weight tolerated before the running maximum is
 // moved (weights enter the PV product as fp16)
 constexpr float kLazyRescale = 8.f;
+// Starting value of the running maximum (log2 units): finite and far below
+// any score q.k * scale * log2(e) of fp16 operands.  A row that has not met
+// a visible key yet keeps it: masked keys then give exp2(-inf) = 0 and
+// rescale factors exp2(floor - m) are 0 (or 1), never inf - inf.  (A part
+// of a split key range can start on a tile that hides every key from some
+// of a wave's rows.)
+constexpr float kMaxFloor = -1e30f;
 
 // LDS layout, chosen for this chip's LDS (128 banks of 4 bytes; a 16-byte
 // access is served 32 lanes at a time): the K tile's 16-byte slot of row r is
@@ -73,7 +80,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p,
   const int h = idx % p.num_q_heads;
   idx /= p.num_q_heads;
   const int c = idx % p.num_chunks;
-  const int qt = num_qtiles - 1 - idx / p.num_chunks;
+  idx /= p.num_chunks;
+  const int sp = idx % p.num_splits;  // part of the key range
+  const int qt = num_qtiles - 1 - idx / p.num_splits;
   const int q_begin = p.cu_q_lens[c], q_end = p.cu_q_lens[c + 1];
   if (q_begin < 0 || q_end > p.total_q || q_end < q_begin) return;
   const int qlen = q_end - q_begin;
@@ -83,7 +92,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p,
   const int P = L - qlen;
   const int Hq = p.num_q_heads;
 
-  if (!(P >= 0 && L >= 1 && L <= p.max_blocks_per_seq * BS)) {
+  if (!(P >= 0 && L >= 1 && L <= p.max_seq_len && L <= p.max_blocks_per_seq * BS)) {
+    if (sp != 0) return;
     for (int i = tid; i < BM * D; i += 256) {
       const int r = row0 + i / D;
       if (r < qlen)
@@ -98,6 +108,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p,
   const int kvh = h / p.group;
   const int kv_end = P + min(row0 + BM, qlen);
   const int ntiles = cdiv(kv_end, BN);
+  // this workgroup's part of the key tiles: [t_lo, t_hi)
+  const int nparts = min(p.num_splits, cdiv(ntiles, p.split_tiles));
+  if (sp >= nparts) return;
+  const int t_lo = sp * ntiles / nparts, t_hi = (sp + 1) * ntiles / nparts;
   const int32_t *trow = p.block_tables + (size_t)c * p.max_blocks_per_seq;
 
   // Tile loader: thread owns keys KPT*lkg .. +KPT-1 and dims 8*lcc .. +7.
@@ -124,7 +138,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p,
     // multiple of KPT); the block id is only meaningful when the first of
     // them lies below L.
     const int pos = t * BN + KPT * lkg;
-    const bool want = t < ntiles && pos < L;
+    const bool want = t < t_hi && pos < L;
     const bool oob = want && (ph < 0 || ph >= p.num_blocks);
     bad |= oob;
     const bool blk = want && !oob;
@@ -168,14 +182,14 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p,
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
     o[dt][0] = o[dt][1] = f4_t{0.f, 0.f, 0.f, 0.f};
-  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+  float m[2] = {kMaxFloor, kMaxFloor}, l[2] = {0.f, 0.f};
 
   if (tid == 0) sBad = 0;
   // Prologue, ordered so that only two memory latencies are exposed: the
   // block ids of tiles 0 and 1, then the query rows (issued while the ids
   // are in flight), then tile 0's K/V, which needs its id.
-  int ph_next = lookup(0);
-  const int ph_one = lookup(1);
+  int ph_next = lookup(t_lo);
+  const int ph_one = lookup(t_lo + 1);
   // The wave's query rows as B operands: column lc of block qb, dims of
   // slot KS*g + kk (8 per slot).  Rows past the chunk load its last row
   // (unconditional loads, nothing waits inside a branch); their results are
@@ -188,15 +202,15 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p,
     for (int kk = 0; kk < KS; ++kk)
       qf[kk][qb] = as_h8(ld16(p.q + ((size_t)(q_begin + qr) * Hq + h) * D + 8 * (KS * g + kk)));
   }
-  load(0, ph_next);
+  load(t_lo, ph_next);
   ph_next = ph_one;
   store(0);
   __syncthreads();
 
   // The wave computes nothing when all its rows lie past the chunk.
   const bool wave_live = wq0 < qlen;
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int buf = kt & 1;
+  for (int kt = t_lo; kt < t_hi; ++kt) {
+    const int buf = (kt - t_lo) & 1;
     const int kbase = kt * BN;
     // the next tile's loads (harmless past the last tile)
     load(kt + 1, ph_next);
@@ -259,9 +273,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p,
         tmax = max_over_rows(vmax(tmax, st[3][qb][3]));
         // Lazy rescaling: the running maximum m only moves when some row's
         // maximum exceeds it by more than 2^8, so weights stay below 256
-        // (exact enough in fp16) and the O rescale is rare.  Key 0 is
-        // visible to every row in the first tile, so m is finite from then
-        // on and exp2(-inf) = 0 removes masked keys.
+        // (exact enough in fp16) and the O rescale is rare.  m starts at a
+        // finite floor, so exp2(-inf) = 0 removes masked keys also in rows
+        // that have not met a visible key yet.
         const float tm = tmax * p.scale_log2e;
         if (__any(tm > m[qb] + kLazyRescale)) {
           const float mnew = fmaxf(m[qb], tm);
@@ -302,30 +316,88 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p,
         o[i % DT][1] = mfma16x16x32(a, pb[i / DT][1], o[i % DT][1]);
       }
     }
-    if (kt + 1 < ntiles) store(buf ^ 1);
+    if (kt + 1 < t_hi) store(buf ^ 1);
     __syncthreads();
   }
 
   if (bad) sBad = 1;
   __syncthreads();
   const bool any_bad = sBad != 0;
+  const f4_t nan4 = f4_t{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
+                         __builtin_nanf("")};
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const float lt = sum_over_rows(l[qb]);
     const int qr = wq0 + 16 * qb + lc;
-    if (qr < qlen) {
-      float *orow = p.out + ((size_t)(q_begin + qr) * Hq + h) * D;
+    if (qr >= qlen) continue;
+    const size_t row = (size_t)(q_begin + qr) * Hq + h;
+    if (nparts == 1) {
+      float *orow = p.out + row * D;
       const float inv = 1.f / lt;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        f4_t r = o[dt][qb] * inv;
-        if (any_bad)
-          r = f4_t{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
-                   __builtin_nanf("")};
-        *reinterpret_cast<f4_t *>(orow + 16 * dt + 4 * g) = r;
+      for (int dt = 0; dt < DT; ++dt)
+        *reinterpret_cast<f4_t *>(orow + 16 * dt + 4 * g) = any_bad ? nan4 : o[dt][qb] * inv;
+    } else {
+      // partial of this part: unnormalised output, row maximum, row sum
+      const size_t prow = (size_t)sp * p.total_q * Hq + row;
+      float *orow = p.ws_o + prow * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        *reinterpret_cast<f4_t *>(orow + 16 * dt + 4 * g) = any_bad ? nan4 : o[dt][qb];
+      if (g == 0) {
+        p.ws_m[prow] = m[qb];
+        p.ws_l[prow] = lt;
       }
     }
   }
+}
+
+// Combines the parts of query tiles whose key range was split: per row,
+// M = max_i m_i, out = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i (the
+// running-maximum rescale of the softmax recurrence, applied across parts).
+// One thread per (row, 4 dims), in one pass: a workgroup takes
+// kMergeRows = 256 / (D/4) consecutive rows of one (query tile, chunk,
+// head), so a query tile is 128 / kMergeRows workgroups.
+template <int D, int BS>
+__global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillParams p, int num_qtiles) {
+  constexpr int BM = 128, BN = 64, D4 = D / 4, kMergeRows = 256 / D4;
+  constexpr int kSubs = BM / kMergeRows;
+  int idx = blockIdx.x;
+  const int sub = idx % kSubs;
+  idx /= kSubs;
+  const int Hq = p.num_q_heads;
+  const int h = idx % Hq;
+  idx /= Hq;
+  const int c = idx % p.num_chunks;
+  const int qt = num_qtiles - 1 - idx / p.num_chunks;
+  const int q_begin = p.cu_q_lens[c], q_end = p.cu_q_lens[c + 1];
+  if (q_begin < 0 || q_end > p.total_q || q_end < q_begin) return;
+  const int qlen = q_end - q_begin;
+  const int row0 = qt * BM;
+  const int qr = row0 + sub * kMergeRows + (int)threadIdx.x / D4;
+  if (qr >= qlen) return;
+  const int L = p.seq_lens[c];
+  const int P = L - qlen;
+  if (!(P >= 0 && L >= 1 && L <= p.max_seq_len && L <= p.max_blocks_per_seq * BS))
+    return;  // the partition kernel wrote NaN
+  const int ntiles = cdiv(P + min(row0 + BM, qlen), BN);
+  const int nparts = min(p.num_splits, cdiv(ntiles, p.split_tiles));
+  if (nparts == 1) return;  // written directly
+  const size_t plane = (size_t)p.total_q * Hq;  // rows of one part
+  const size_t row = (size_t)(q_begin + qr) * Hq + h;
+  const int d = 4 * ((int)threadIdx.x % D4);
+  float M = p.ws_m[row];
+#pragma unroll 4
+  for (int j = 1; j < nparts; ++j) M = fmaxf(M, p.ws_m[j * plane + row]);
+  f4_t o = f4_t{0.f, 0.f, 0.f, 0.f};
+  float l = 0.f;
+#pragma unroll 4
+  for (int j = 0; j < nparts; ++j) {
+    const float e = fast_exp2(p.ws_m[j * plane + row] - M);
+    o += e * *reinterpret_cast<const f4_t *>(p.ws_o + (j * plane + row) * D + d);
+    l += e * p.ws_l[j * plane + row];
+  }
+  *reinterpret_cast<f4_t *>(p.out + row * D + d) = o * (1.f / l);
 }
 
 template <int D, int BS>
@@ -333,9 +405,17 @@ static hipError_t launch(const PrefillParams &p, int max_q_len,
                          hipStream_t stream) {
   if (p.num_chunks == 0 || max_q_len == 0) return hipSuccess;
   const int qtiles = cdiv(max_q_len, 128);
-  const int64_t grid = (int64_t)qtiles * p.num_chunks * p.num_q_heads;
-  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  const int64_t tiles = (int64_t)qtiles * p.num_chunks * p.num_q_heads;
+  const int64_t grid = tiles * p.num_splits;
+  constexpr int kMergeSubs = 128 / (256 / (D / 4));  // merge workgroups per query tile
+  if (grid > 0x7fffffff || tiles * kMergeSubs > 0x7fffffff || p.num_splits < 1 ||
+      p.split_tiles < 1)
+    return hipErrorInvalidValue;
   prefill_kernel<D, BS><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(p, qtiles);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.num_splits == 1) return e;
+  prefill_merge_kernel<D, BS>
+      <<<dim3((unsigned)(tiles * kMergeSubs)), dim3(256), 0, stream>>>(p, qtiles);
   return hipGetLastError();
 }
 

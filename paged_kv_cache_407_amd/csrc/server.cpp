@@ -10,8 +10,8 @@
 // pkv_server_execute: enqueues pkv_kv_append of the step's new rows, the
 // prefill of its chunks and the decode of its decode rows, reading the
 // plan from the device copy.
-// Staging and workspace are allocated once, when the server is created; the
-// caller owns the pools, the new rows and the outputs.
+// Staging and the attention workspace are allocated once, when the server
+// is created; the caller owns the pools, the new rows and the outputs.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -86,10 +86,19 @@ pkv_server *pkv_server_create(pkv_scheduler *sched, pkv_block_manager *bm, void 
   s->o_dl = s->o_dt + B * MB;
   s->o_sl = s->o_dl + B;
   s->n_ints = s->o_sl + s->T + B;
-  // The decode workspace for the smallest partition the library picks.
+  // One workspace serves the step's prefill and decode, which run in turn
+  // on one stream.  Decode: the smallest partition the library picks.
+  // Prefill: a single chunk of t tokens is split at least as far as any
+  // batch of t tokens, and within one 128-row tile count the size grows
+  // with t, so the largest need is at a multiple of 128 or at T.
   const int32_t min_part = std::min(256, 64 * s->bs) / s->bs * s->bs;
   s->ws_bytes = pkv_decode_workspace_size(s->B, s->Hq, s->Hkv, s->D, s->bs, max_seq_len,
                                           min_part);
+  for (int32_t t = std::min(128, s->T);; t = std::min(t + 128, s->T)) {
+    s->ws_bytes = std::max(
+        s->ws_bytes, pkv_prefill_workspace_size(1, t, t, s->Hq, s->D, max_seq_len));
+    if (t == s->T) break;
+  }
   bool ok = (s->ids = new (std::nothrow) int64_t[4 * B]) != nullptr;
   for (int i = 0; i < 2 && ok; ++i)
     ok = hipHostMalloc((void **)&s->host[i], s->n_ints * 4, hipHostMallocDefault) ==
@@ -172,7 +181,8 @@ int pkv_server_execute(pkv_server *s, const void *new_k, const void *new_v, cons
     rc = pkv_paged_attention_prefill(out_prefill, q, d + s->o_cu, s->k_cache, s->v_cache,
                                      d + s->o_pt, d + s->o_pl, p.num_prefill,
                                      p.num_prefill_tokens, max_q, s->Hq, s->Hkv, s->D, s->bs,
-                                     s->NB, s->MB, s->scale, stream);
+                                     s->NB, s->MB, s->max_seq_len, s->scale, s->ws,
+                                     s->ws_bytes, stream);
     if (rc != PKV_OK) return rc;
   }
   if (p.num_decode) {

@@ -69,7 +69,7 @@ class DevBatch:
             self.q_pf, self.cu, self.k_cache if k_cache is None else k_cache,
             self.v_cache if v_cache is None else v_cache,
             self.tables_pf if tables is None else tables, self.lens_pf,
-            max_q_len=self.max_q, scale=self.b.scale)
+            max_q_len=self.max_q, max_seq_len=int(self.b.lens_pf.max()), scale=self.b.scale)
 
 
 def max_abs(a, b) -> float:

@@ -23,7 +23,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("pkv_kv_append", "pkv_paged_attention_decode",
               "pkv_paged_attention_prefill", "pkv_status_string",
-              "pkv_decode_workspace_size"):
+              "pkv_decode_workspace_size", "pkv_prefill_workspace_size"):
         assert n in names
 
 
@@ -102,12 +102,31 @@ def test_invalid_arguments_are_rejected_on_the_host():
     assert dec(P, P, P, P, P, P, 2, 4, 4, 128, 16, 8, 4, 64, 0.0, 0, None, 0, None) == 1
     assert dec(P, P, P, P, P, P, 2, 4, 4, 128, 16, 8, 4, 64, -0.1, 0, None, 0, None) == 1
     pre = lib.pkv_paged_attention_prefill
-    assert pre(P, P, P, P, P, P, P, 1, 8, 8, 4, 3, 128, 16, 8, 4, 0.1, None) == 1
-    assert pre(P, P, P, P, P, P, P, 1, 8, 8, 4, 4, 80, 16, 8, 4, 0.1, None) == 2
+    assert pre(P, P, P, P, P, P, P, 1, 8, 8, 4, 3, 128, 16, 8, 4, 64, 0.1, None, 0, None) == 1
+    assert pre(P, P, P, P, P, P, P, 1, 8, 8, 4, 4, 80, 16, 8, 4, 64, 0.1, None, 0, None) == 2
     # block size 1 is a decode-only instance
-    assert pre(P, P, P, P, P, P, P, 1, 8, 8, 4, 4, 128, 1, 8, 4, 0.1, None) == 2
-    assert pre(P, P, P, P, P, P, P, 1, 8, 8, 4, 4, 128, 16, 8, 4, -1.0, None) == 1
-    assert pre(None, None, None, None, None, None, None, 0, 0, 0, 4, 4, 128, 16, 8, 4, 0.1, None) == 0
+    assert pre(P, P, P, P, P, P, P, 1, 8, 8, 4, 4, 128, 1, 8, 4, 4, 0.1, None, 0, None) == 2
+    assert pre(P, P, P, P, P, P, P, 1, 8, 8, 4, 4, 128, 16, 8, 4, 64, -1.0, None, 0, None) == 1
+    # max_seq_len beyond the table
+    assert pre(P, P, P, P, P, P, P, 1, 8, 8, 4, 4, 128, 16, 8, 4, 65, 0.1, None, 0, None) == 1
+    # a split key range needs the workspace
+    assert pre(P, P, P, P, P, P, P, 1, 8, 8, 4, 4, 128, 16, 8, 256, 4096, 0.1, None, 0,
+               None) == 1
+    assert pre(None, None, None, None, None, None, None, 0, 0, 0, 4, 4, 128, 16, 8, 4, 64, 0.1,
+               None, 0, None) == 0
+
+
+def test_prefill_workspace_size():
+    """One 128-row query tile per head (4 heads) is far below the target
+    grid: a 4096-token key range (64 key tiles) splits into 16 parts of 4
+    tiles, each part holding float o[8 tokens][4 heads][128], m and l; a
+    single key tile is never split."""
+    lib = pkv.load_library()
+    ws = lib.pkv_prefill_workspace_size
+    rows = 16 * 8 * 4
+    assert ws(1, 8, 8, 4, 128, 4096) == rows * 128 * 4 + 2 * rows * 4
+    assert ws(1, 8, 8, 4, 128, 64) == 0
+    assert ws(0, 8, 8, 4, 128, 4096) == 0
 
 
 def test_binding_refuses_cpu_tensors():

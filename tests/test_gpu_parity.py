@@ -373,6 +373,94 @@ def test_prefill_bad_chunk_is_nan():
     assert np.array_equal(out[rest].view(np.uint32), good[rest].view(np.uint32))
 
 
+# ------------------------------------------------- split key ranges (prefill)
+# Few query tiles on long prefixes: the library cuts each query tile's key
+# range into parts run by different workgroups and merges them.  The chunk on
+# an empty prefix has too few key tiles to split and is written directly in
+# the same launch.
+SPLIT_PREFIXES = [2000, 0, 900, 1500]
+SPLIT_CHUNK = 70
+
+
+def split_spec(D, bs, Hq, Hkv, seed):
+    L = [p + SPLIT_CHUNK for p in SPLIT_PREFIXES]
+    return W.Spec(name=f"split_d{D}_bs{bs}_{Hq}_{Hkv}", num_q_heads=Hq, num_kv_heads=Hkv,
+                  head_dim=D, block_size=bs,
+                  num_blocks=sum(W.cdiv(x, bs) for x in L) + 2 * W.cdiv(100, bs) + 16,
+                  seed=seed, decode_count=2, decode_dist="uniform", decode_lo=1, decode_hi=100,
+                  prefill_chunks=len(L), prefill_chunk_len=SPLIT_CHUNK,
+                  max_blocks_per_seq=W.cdiv(max(L), bs))
+
+
+def split_call(b, dev, max_seq_len, tables=None, workspace=None):
+    return to_host(pkv.paged_attention_prefill(
+        dev.q_pf, dev.cu, dev.k_cache, dev.v_cache,
+        dev.tables_pf if tables is None else tables, dev.lens_pf, max_q_len=SPLIT_CHUNK,
+        max_seq_len=max_seq_len, scale=b.scale, workspace=workspace))
+
+
+@pytest.mark.parametrize("D,bs,Hq,Hkv", [(128, 16, 2, 1), (64, 8, 4, 4), (128, 32, 4, 2),
+                                         (128, 8, 2, 2), (64, 16, 2, 1)],
+                         ids=lambda x: str(x))
+def test_prefill_split_key_ranges(D, bs, Hq, Hkv):
+    spec = split_spec(D, bs, Hq, Hkv, seed=D + bs + Hq)
+    say("prefill split", spec.name)
+    b = W.make_batch(spec, lens_override={"prefix": SPLIT_PREFIXES})
+    T = b.q_pf.shape[0]
+    maxl = int(b.lens_pf.max())
+    need = pkv.prefill_workspace_size(len(SPLIT_PREFIXES), T, SPLIT_CHUNK, Hq, D, maxl)
+    assert need > 0                      # the call takes the split path
+    dev = DevBatch(b)
+    dev.append()
+    kc, vc = check_append(b, dev)
+    # a workspace holding NaN bit patterns: its contents on entry do not matter
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    out = split_call(b, dev, maxl, workspace=ws)
+    check_prefill(b, kc, vc, out)
+    # a looser bound on the lengths cuts the key ranges differently
+    out2 = split_call(b, dev, spec.max_blocks_per_seq * bs)
+    check_prefill(b, kc, vc, out2)
+    # the same call again on the same workspace is bitwise repeatable
+    assert np.array_equal(split_call(b, dev, maxl, workspace=ws).view(np.uint32),
+                          out.view(np.uint32))
+
+
+def test_prefill_split_bad_block_and_short_bound():
+    spec = split_spec(128, 16, 2, 1, seed=77)
+    b = W.make_batch(spec, lens_override={"prefix": SPLIT_PREFIXES})
+    dev = DevBatch(b)
+    dev.append()
+    maxl = int(b.lens_pf.max())
+    good = split_call(b, dev, maxl)
+    cu = b.cu_q_lens
+    rows = lambda c: np.r_[int(cu[c]):int(cu[c + 1])]
+    # an out-of-range block id in the middle of chunk 0's prefix (one part of
+    # its split key range) turns the chunk's rows to NaN, nothing else
+    tab = b.tables_pf.copy()
+    tab[0, 60] = spec.num_blocks + 5
+    bad = split_call(b, dev, maxl, tables=to_dev(tab))
+    assert np.isnan(bad[rows(0)]).all()
+    rest = np.r_[int(cu[1]):bad.shape[0]]
+    assert np.array_equal(bad[rest].view(np.uint32), good[rest].view(np.uint32))
+    # chunks longer than max_seq_len get NaN rows; the others stay exact
+    short = split_call(b, dev, 1000)
+    kc, vc = to_host(dev.k_cache), to_host(dev.v_cache)
+    for c, L in enumerate(b.lens_pf):
+        if L > 1000:
+            assert np.isnan(short[rows(c)]).all()
+        else:
+            assert not np.isnan(short[rows(c)]).any()
+    keep = [c for c, L in enumerate(b.lens_pf) if L <= 1000]
+    ref = oracle.prefill(b.q_pf, b.cu_q_lens, kc, vc, b.tables_pf, b.lens_pf, b.scale)
+    for c in keep:
+        assert max_abs(short[rows(c)], ref[rows(c)]) <= TOL
+    # a workspace below the size the call needs is refused
+    need = pkv.prefill_workspace_size(4, b.q_pf.shape[0], SPLIT_CHUNK, 2, 128, maxl)
+    with pytest.raises(pkv.PkvError):
+        split_call(b, dev, maxl, workspace=torch.empty(need - 256, dtype=torch.uint8,
+                                                      device="cuda"))
+
+
 # --------------------------------------------- grouped heads, workspace reuse
 @pytest.mark.parametrize("Hq,Hkv", [(6, 2), (12, 2), (12, 1), (16, 1), (6, 6)],
                          ids=lambda x: str(x))
