@@ -386,16 +386,38 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillParams p, int
   const size_t plane = (size_t)p.total_q * Hq;  // rows of one part
   const size_t row = (size_t)(q_begin + qr) * Hq + h;
   const int d = 4 * ((int)threadIdx.x % D4);
-  float M = p.ws_m[row];
-#pragma unroll 4
-  for (int j = 1; j < nparts; ++j) M = fmaxf(M, p.ws_m[j * plane + row]);
+  // kChunk parts at a time in one online pass, all loads of a chunk issued
+  // together (a part index past the last is clamped to part 0, its values
+  // unused); part 0 holds key 0, which every row sees, so m_0 is a score.
+  constexpr int kChunk = 4;
+  float M = -INFINITY, l = 0.f;
   f4_t o = f4_t{0.f, 0.f, 0.f, 0.f};
-  float l = 0.f;
-#pragma unroll 4
-  for (int j = 0; j < nparts; ++j) {
-    const float e = fast_exp2(p.ws_m[j * plane + row] - M);
-    o += e * *reinterpret_cast<const f4_t *>(p.ws_o + (j * plane + row) * D + d);
-    l += e * p.ws_l[j * plane + row];
+  for (int j0 = 0; j0 < nparts; j0 += kChunk) {
+    float mj[kChunk], lj[kChunk];
+    f4_t oj[kChunk];
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) {
+      const size_t pr = (size_t)(j0 + u < nparts ? j0 + u : 0) * plane + row;
+      mj[u] = p.ws_m[pr];
+      lj[u] = p.ws_l[pr];
+      oj[u] = *reinterpret_cast<const f4_t *>(p.ws_o + pr * D + d);
+    }
+    float cm = M;
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u)
+      if (j0 + u < nparts) cm = fmaxf(cm, mj[u]);
+    const float a = fast_exp2(M - cm);  // 0 on the first chunk (M = -inf)
+    o *= a;
+    l *= a;
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) {
+      if (j0 + u < nparts) {
+        const float e = fast_exp2(mj[u] - cm);
+        o += e * oj[u];
+        l += e * lj[u];
+      }
+    }
+    M = cm;
   }
   *reinterpret_cast<f4_t *>(p.out + row * D + d) = o * (1.f / l);
 }
