@@ -67,6 +67,9 @@ def parse():
                     help="time the decode of the workload's batch at block sizes 1, 8, "
                          "16 and 32 (same lengths and pool capacity in tokens) and "
                          "print one JSON line per block size")
+    ap.add_argument("--prefill-sweep", action="store_true",
+                    help="time prefill alone on batches of few query tiles over long "
+                         "prefixes (the key-range split) and on the mixed step's chunks")
     ap.add_argument("--swap-bench", action="store_true",
                     help="time swapping blocks of the workload's shape out to a pinned "
                          "host pool and back (kernel and DMA paths); one JSON line per "
@@ -220,6 +223,9 @@ def main():
     log("library", pkv.LIB_PATH, "device", torch.cuda.get_device_name(dev))
     if args.block_size_sweep:
         block_size_sweep(args, dev)
+        return
+    if args.prefill_sweep:
+        prefill_sweep(args, dev)
         return
     if args.swap_bench:
         swap_bench(args, dev)
@@ -506,6 +512,92 @@ def block_size_sweep(args, dev):
             "us_p90": round(float(np.percentile(d, 90)), 3),
             "alg_bytes": alg, "GBps": round(gbs, 1),
             "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "calls": n, "replicas": R}),
+            flush=True)
+        del reps
+        torch.cuda.empty_cache()
+
+
+# (label, chunks, new tokens per chunk, prefix lo, prefix hi) at the 32 x 128
+# MHA shape with block size 16
+PREFILL_SWEEP = [
+    ("1 chunk x 512 on a 3584-token prefix", 1, 512, 3584, 3584),
+    ("1 chunk x 512 on a 1536-token prefix", 1, 512, 1536, 1536),
+    ("2 chunks x 256 on prefixes U[1024,2048]", 2, 256, 1024, 2048),
+    ("1 chunk x 2048 on an empty prefix", 1, 2048, 0, 0),
+    ("4 chunks x 512 on prefixes U[0,512]", 4, 512, 0, 512),
+]
+
+
+def prefill_sweep(args, dev):
+    """Prefill alone on batches whose query tiles are few (one or two
+    chunks on long prefixes: the library cuts their key ranges across
+    workgroups and merges the parts) and on the mixed step's 4 chunks
+    (not split).  Per-call HIP-event times, caches cold across replicas."""
+    import torch
+    import paged_kv_cache_407_amd as pkv
+    base = W.SPECS["mixed"]
+    for i, (label, C, clen, plo, phi) in enumerate(PREFILL_SWEEP):
+        spec = W.Spec(name=f"prefill_sweep_{i}", num_q_heads=base.num_q_heads,
+                      num_kv_heads=base.num_kv_heads, head_dim=base.head_dim,
+                      block_size=base.block_size,
+                      num_blocks=C * W.cdiv(clen + phi, base.block_size) + 8,
+                      seed=W.SEED_BASE + 20 + i, prefill_chunks=C, prefill_chunk_len=clen,
+                      prefill_prefix_lo=plo, prefill_prefix_hi=phi)
+        b = W.make_batch(spec)
+        T, Hq, D = b.q_pf.shape
+        max_q = int(np.diff(b.cu_q_lens).max())
+        max_len = int(b.lens_pf.max())
+        flops = W.prefill_flops(b)
+        wsb = pkv.prefill_workspace_size(C, T, max_q, Hq, D, max_len)
+        R = max(1, min(8, int(16e9 // b.nbytes_pool())))
+
+        def to_dev(a):
+            a = np.ascontiguousarray(a)
+            if a.dtype == np.float16:
+                return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.float16)
+            return torch.from_numpy(a).to(dev)
+        nk, nv, slots = to_dev(b.new_k), to_dev(b.new_v), to_dev(b.slot_mapping)
+        q, cu = to_dev(b.q_pf), to_dev(b.cu_q_lens)
+        tab, lens = to_dev(b.tables_pf), to_dev(b.lens_pf)
+        out = torch.empty((T, Hq, D), dtype=torch.float32, device=dev)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
+        reps = []
+        for r in range(R):
+            kc, vc = to_dev(b.k_cache), to_dev(b.v_cache)
+            pkv.kv_append(nk, nv, kc, vc, slots)
+            reps.append((kc, vc))
+
+        def call(rep):
+            pkv.paged_attention_prefill(q, cu, rep[0], rep[1], tab, lens, max_q_len=max_q,
+                                        max_seq_len=max_len, scale=b.scale, out=out,
+                                        workspace=ws)
+        for j in range(args.warmup):
+            call(reps[j % R])
+        n = max(args.steps, 20)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n)]
+        torch.cuda.synchronize()
+        torch.cuda._sleep(200_000_000)
+        for j, (e0, e1) in enumerate(ev):
+            e0.record()
+            call(reps[j % R])
+            e1.record()
+        torch.cuda.synchronize()
+        d = np.array([e0.elapsed_time(e1) for e0, e1 in ev]) * 1e3
+        tf = flops / (d.mean() * 1e-6) / 1e12
+        log(f"{label}: prefill {d.mean():8.2f} us, {tf:6.1f} TFLOP/s "
+            f"({100 * tf / MFMA_F16_PEAK_TFLOPS:5.1f} % of fp16 MFMA peak), "
+            f"{'split, workspace %.1f MiB' % (wsb / 2**20) if wsb else 'not split'}")
+        print(json.dumps({
+            "metric": "paged causal prefill TFLOP/s", "case": label, "chunks": C,
+            "chunk_len": clen, "prefixes": (b.lens_pf - clen).tolist(),
+            "num_q_heads": Hq, "num_kv_heads": spec.num_kv_heads, "head_dim": D,
+            "block_size": spec.block_size, "flops": flops,
+            "us_mean": round(float(d.mean()), 3),
+            "us_p10": round(float(np.percentile(d, 10)), 3),
+            "us_p90": round(float(np.percentile(d, 90)), 3),
+            "tflops": round(tf, 1), "frac_mfma_f16_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
+            "split": bool(wsb), "workspace_bytes": wsb, "calls": n, "replicas": R}),
             flush=True)
         del reps
         torch.cuda.empty_cache()
