@@ -14,10 +14,11 @@ using namespace pkv;
 namespace {
 
 // Default split: the largest partition (1024, 512 or 256 tokens, at most 64
-// blocks) that still gives at least kTargetWorkgroups decode workgroups, so
-// long sequences run few, long workgroups and short batches still fill the
-// chip's 256 CUs several times over.
-constexpr int kTargetWorkgroups = 4096;
+// blocks) that still gives at least kTargetWorkgroups decode workgroups of 8
+// waves (4 per CU on the chip's 256 CUs), so long sequences run few, long
+// workgroups, a batch that fills the chip is not split (no merge launch),
+// and short batches are cut until they fill it.
+constexpr int kTargetWorkgroups = 1024;
 constexpr int kPartitionChoices[] = {1024, 512, 256};
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
@@ -87,10 +88,11 @@ int hip_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_HIP; }
 // part of the chip idles while each workgroup walks its whole key range.
 // The key range of a query tile is then cut into parts of at least
 // kMinSplitTiles tiles until the grid reaches about that many workgroups.
-// Larger grids are not split: the parts' partial outputs cost a write and a
-// read of fp32 rows, which a full chip does not win back.
+// Larger grids are not split, and a part holds at least kMinSplitTiles key
+// tiles: the parts' partial outputs cost a write and a read of fp32 rows
+// and a second launch, which shorter chains do not win back.
 constexpr int kPrefillTargetWorkgroups = 512;
-constexpr int kMinSplitTiles = 4;
+constexpr int kMinSplitTiles = 8;
 
 struct PrefillSplit {
   int32_t parts = 1, tiles = 1;

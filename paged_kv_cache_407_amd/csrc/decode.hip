@@ -46,10 +46,11 @@ namespace pkv {
 // moved
 constexpr float kLazyRescale = 8.f;
 
-// Tuning constants: waves per workgroup, and 16-byte K loads per lane in one
-// wave step (the same number of V loads is in flight beside them).
+// Tuning constants: waves per workgroup (where a partition holds enough wave
+// steps), and 16-byte K loads per lane in one wave step (the same number of V
+// loads is in flight beside them).
 #ifndef PKV_DECODE_WAVES
-#define PKV_DECODE_WAVES 4
+#define PKV_DECODE_WAVES 8
 #endif
 #ifndef PKV_DECODE_STEP_LOADS
 #define PKV_DECODE_STEP_LOADS 8
@@ -72,13 +73,18 @@ struct DecodeShape {
                                 : (LPB >= kStepLoads ? LPB : (kStepLoads / LPB) * LPB);
   static constexpr int BPS = NL * RPL / BS;       // blocks per wave step
   static_assert(SUB ? RPL % BS == 0 : BS % RPL == 0, "blocks and loads nest");
+  // Waves per workgroup: a partition holds at most kMaxPartBlocks blocks, so
+  // with blocks smaller than a wave-wide load it holds only a few wave steps
+  // (2 at head_dim 128, 1 at 64); more waves would idle.
+  static constexpr int STEPS = kMaxPartBlocks / BPS;  // wave steps per partition
+  static constexpr int NW = STEPS < kDecodeWaves ? (STEPS > 0 ? STEPS : 1) : kDecodeWaves;
 };
 
 template <int D, int BS, int GH>
-__global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeParams p) {
+__global__ __launch_bounds__((64 * DecodeShape<D, BS>::NW)) void decode_kernel(DecodeParams p) {
   using Sh = DecodeShape<D, BS>;
   constexpr int LPR = Sh::LPR, RPL = Sh::RPL, LPB = Sh::LPB, BPS = Sh::BPS,
-                NL = Sh::NL, NW = kDecodeWaves;
+                NL = Sh::NL, NW = Sh::NW;
   constexpr bool SUB = Sh::SUB;
   __shared__ float s_acc[NW][GH][D];
   __shared__ float s_m[NW][GH], s_l[NW][GH];
@@ -529,7 +535,7 @@ static hipError_t launch(const DecodeParams &p, hipStream_t stream) {
     decode_gqa8_kernel<D, BS><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(p);
   else
     decode_kernel<D, BS, GH>
-        <<<dim3((unsigned)grid), dim3(64 * kDecodeWaves), 0, stream>>>(p);
+        <<<dim3((unsigned)grid), dim3(64 * DecodeShape<D, BS>::NW), 0, stream>>>(p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.num_parts == 1) return e;
   const int64_t rows = (int64_t)p.num_seqs * p.num_q_heads;

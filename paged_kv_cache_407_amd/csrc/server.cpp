@@ -175,14 +175,17 @@ int pkv_server_execute(pkv_server *s, const void *new_k, const void *new_v, cons
   if (rc != PKV_OK) return rc;
   const size_t qrow = (size_t)s->Hq * s->D * 2;  // bytes of one query row
   if (p.num_prefill) {
-    int32_t max_q = 0;
-    for (int32_t k = 0; k < p.num_prefill; ++k)
+    // the step's own bounds: the split of the chunks' key ranges follows them
+    int32_t max_q = 0, max_len = 0;
+    for (int32_t k = 0; k < p.num_prefill; ++k) {
       max_q = std::max(max_q, h[s->o_cu + k + 1] - h[s->o_cu + k]);
+      max_len = std::max(max_len, h[s->o_pl + k]);
+    }
     rc = pkv_paged_attention_prefill(out_prefill, q, d + s->o_cu, s->k_cache, s->v_cache,
                                      d + s->o_pt, d + s->o_pl, p.num_prefill,
                                      p.num_prefill_tokens, max_q, s->Hq, s->Hkv, s->D, s->bs,
-                                     s->NB, s->MB, s->max_seq_len, s->scale, s->ws,
-                                     s->ws_bytes, stream);
+                                     s->NB, s->MB, max_len, s->scale, s->ws, s->ws_bytes,
+                                     stream);
     if (rc != PKV_OK) return rc;
   }
   if (p.num_decode) {

@@ -56,11 +56,14 @@ def test_partition_and_workspace_policy():
     # short sequences are not split and need no workspace
     assert pkv.decode_partition_size(32, 32, 32, 128, 16, 200) == 208
     assert pkv.decode_workspace_size(32, 32, 32, 128, 16, 200) == 0
-    # long ones are split: the largest of 1024 / 512 / 256 tokens that still
-    # gives at least 4096 workgroups
+    # the largest of 1024 / 512 / 256 tokens that still gives at least 1024
+    # workgroups; a sequence that fits one partition is not split
     assert pkv.decode_partition_size(8, 32, 32, 128, 16, 32768) == 1024      # 8 x 32K
-    assert pkv.decode_partition_size(60, 32, 32, 128, 16, 2031) == 512       # mixed step
-    assert pkv.decode_partition_size(32, 32, 32, 128, 16, 1017) == 256       # batch 32
+    assert pkv.decode_partition_size(60, 32, 32, 128, 16, 2031) == 1024      # mixed step
+    assert pkv.decode_partition_size(32, 32, 32, 128, 16, 1017) == 1024      # batch 32
+    assert pkv.decode_workspace_size(32, 32, 32, 128, 16, 1017) == 0
+    assert pkv.decode_partition_size(4, 32, 32, 128, 16, 1017) == 256        # batch 4
+    assert pkv.decode_partition_size(8, 32, 32, 128, 16, 2048) == 512        # batch 8
     assert pkv.decode_partition_size(256, 64, 8, 128, 32, 4096) == 1024      # GQA 64/8
     ws = pkv.decode_workspace_size(8, 32, 32, 128, 16, 32768)
     rows = 8 * 32 * 32
@@ -118,13 +121,14 @@ def test_invalid_arguments_are_rejected_on_the_host():
 
 def test_prefill_workspace_size():
     """One 128-row query tile per head (4 heads) is far below the target
-    grid: a 4096-token key range (64 key tiles) splits into 16 parts of 4
+    grid: a 4096-token key range (64 key tiles) splits into 8 parts of 8
     tiles, each part holding float o[8 tokens][4 heads][128], m and l; a
-    single key tile is never split."""
+    range of 8 key tiles or fewer is never split."""
     lib = pkv.load_library()
     ws = lib.pkv_prefill_workspace_size
-    rows = 16 * 8 * 4
+    rows = 8 * 8 * 4
     assert ws(1, 8, 8, 4, 128, 4096) == rows * 128 * 4 + 2 * rows * 4
+    assert ws(1, 8, 8, 4, 128, 512) == 0
     assert ws(1, 8, 8, 4, 128, 64) == 0
     assert ws(0, 8, 8, 4, 128, 4096) == 0
 
