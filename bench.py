@@ -197,6 +197,34 @@ def measured_traffic(workload: str):
         return None
 
 
+def event_times(call, n):
+    """Times call(i), i = 0..n-1, on the current stream: (per-call HIP-event
+    times, mean launch duration), in us.  The mean is one event pair around
+    n back-to-back launches divided by n -- the kernels' average duration
+    plus the gaps between them, as a profiler sees them; the per-call pairs
+    add each event's own overhead and give the spread.  The GPU is kept
+    ahead of the host in both."""
+    import torch
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(200_000_000)
+    for i in range(n):
+        starts[i].record()
+        call(i)
+        ends[i].record()
+    torch.cuda.synchronize()
+    d = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)]) * 1e3
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(200_000_000)
+    e0.record()
+    for i in range(n):
+        call(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return d, e0.elapsed_time(e1) * 1e3 / n
+
+
 def main():
     args = parse()
     if args.summarize_pmc:
@@ -359,25 +387,13 @@ def main():
 
     # per-call durations with events (GPU kept ahead of the host by a spin)
     def timed_calls(fn, n):
-        starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
-        ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
-        torch.cuda.synchronize()
-        torch.cuda._sleep(200_000_000)
-        for i in range(n):
-            rep = reps[i % R]
-            starts[i].record()
-            fn(rep)
-            ends[i].record()
-        torch.cuda.synchronize()
-        d = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)]) * 1e3  # us
-        return d
+        return event_times(lambda i: fn(reps[i % R]), n)
 
     n_inst = min(K, 200)
     res = {}
     if S:
-        d = timed_calls(do_decode, n_inst)
-        res["decode_us"] = d
-    d_app = timed_calls(do_append, n_inst)
+        res["decode_us"] = timed_calls(do_decode, n_inst)
+    d_app, app_mean = timed_calls(do_append, n_inst)
     if C:
         res["prefill_us"] = timed_calls(do_prefill, n_inst)
 
@@ -410,24 +426,27 @@ def main():
         "kv_bytes_per_step": kv_bytes,
         "kv_bytes_logical": kvb["logical"],
         "wall_ms_per_step": round(wall_ms / K, 6),
-        "append_us_mean": round(float(d_app.mean()), 3),
+        "append_us_mean": round(app_mean, 3),
     }
     if S:
-        d = res["decode_us"]
-        achieved = decode_alg_bytes / (d.mean() * 1e-6) / 1e9
+        d, mean = res["decode_us"]
+        achieved = decode_alg_bytes / (mean * 1e-6) / 1e9
         line["roofline"] = {
             "kernel": "paged_attention_decode (partition kernel + merge kernel when split)",
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(args.workload),
             "alg_bytes_per_launch": decode_alg_bytes,
-            "us_mean": round(float(d.mean()), 3), "us_p10": round(float(np.percentile(d, 10)), 3),
+            "us_mean": round(mean, 3),
+            "us_mean_per_call_events": round(float(d.mean()), 3),
+            "us_p10": round(float(np.percentile(d, 10)), 3),
             "us_p90": round(float(np.percentile(d, 90)), 3),
         }
     if C:
-        d = res["prefill_us"]
-        tf = pf_flops / (d.mean() * 1e-6) / 1e12
-        line["prefill"] = {"flops": pf_flops, "us_mean": round(float(d.mean()), 3),
+        d, mean = res["prefill_us"]
+        tf = pf_flops / (mean * 1e-6) / 1e12
+        line["prefill"] = {"flops": pf_flops, "us_mean": round(mean, 3),
+                           "us_mean_per_call_events": round(float(d.mean()), 3),
                            "tflops": round(tf, 1),
                            "frac_mfma_f16_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
                            "tokens_per_s": round(int(b.new_k.shape[0]) / step_s, 1)}
@@ -445,7 +464,7 @@ def block_size_sweep(args, dev):
     queries and KV contents, the pool holding the same number of tokens
     (num_blocks * block_size fixed), each block table as wide as the longest
     sequence needs.  Cold caches as in the main run (replicas), per-call
-    HIP-event times with the GPU kept ahead of the host."""
+    launch durations (event_times) with the GPU kept ahead of the host."""
     import dataclasses
     import torch
     import paged_kv_cache_407_amd as pkv
@@ -489,25 +508,17 @@ def block_size_sweep(args, dev):
         for i in range(args.warmup):
             call(reps[i % R])
         n = max(args.steps, 20)
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(n)]
-        torch.cuda.synchronize()
-        torch.cuda._sleep(200_000_000)
-        for i, (e0, e1) in enumerate(ev):
-            e0.record()
-            call(reps[i % R])
-            e1.record()
-        torch.cuda.synchronize()
-        d = np.array([e0.elapsed_time(e1) for e0, e1 in ev]) * 1e3
-        gbs = alg / (d.mean() * 1e-6) / 1e9
-        log(f"block size {bs:2d}: decode {d.mean():8.2f} us, {gbs:7.1f} GB/s "
+        d, mean = event_times(lambda i: call(reps[i % R]), n)
+        gbs = alg / (mean * 1e-6) / 1e9
+        log(f"block size {bs:2d}: decode {mean:8.2f} us, {gbs:7.1f} GB/s "
             f"({100 * gbs / HBM_PEAK_GBS:5.1f} % of HBM peak), partition {part}, "
             f"table width {b.tables_dec.shape[1]}, replicas {R}")
         print(json.dumps({
             "metric": "paged decode GB/s by block size", "workload": args.workload,
             "block_size": bs, "num_blocks": spec.num_blocks,
             "table_entries": int(sum(W.cdiv(int(L), bs) for L in b.lens_dec)),
-            "partition_size": part, "us_mean": round(float(d.mean()), 3),
+            "partition_size": part, "us_mean": round(mean, 3),
+            "us_mean_per_call_events": round(float(d.mean()), 3),
             "us_p10": round(float(np.percentile(d, 10)), 3),
             "us_p90": round(float(np.percentile(d, 90)), 3),
             "alg_bytes": alg, "GBps": round(gbs, 1),
@@ -532,7 +543,8 @@ def prefill_sweep(args, dev):
     """Prefill alone on batches whose query tiles are few (one or two
     chunks on long prefixes: the library cuts their key ranges across
     workgroups and merges the parts) and on the mixed step's 4 chunks
-    (not split).  Per-call HIP-event times, caches cold across replicas."""
+    (not split).  Launch durations as event_times measures them, caches cold
+    across replicas."""
     import torch
     import paged_kv_cache_407_amd as pkv
     base = W.SPECS["mixed"]
@@ -574,18 +586,9 @@ def prefill_sweep(args, dev):
         for j in range(args.warmup):
             call(reps[j % R])
         n = max(args.steps, 20)
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(n)]
-        torch.cuda.synchronize()
-        torch.cuda._sleep(200_000_000)
-        for j, (e0, e1) in enumerate(ev):
-            e0.record()
-            call(reps[j % R])
-            e1.record()
-        torch.cuda.synchronize()
-        d = np.array([e0.elapsed_time(e1) for e0, e1 in ev]) * 1e3
-        tf = flops / (d.mean() * 1e-6) / 1e12
-        log(f"{label}: prefill {d.mean():8.2f} us, {tf:6.1f} TFLOP/s "
+        d, mean = event_times(lambda j: call(reps[j % R]), n)
+        tf = flops / (mean * 1e-6) / 1e12
+        log(f"{label}: prefill {mean:8.2f} us, {tf:6.1f} TFLOP/s "
             f"({100 * tf / MFMA_F16_PEAK_TFLOPS:5.1f} % of fp16 MFMA peak), "
             f"{'split, workspace %.1f MiB' % (wsb / 2**20) if wsb else 'not split'}")
         print(json.dumps({
@@ -593,7 +596,8 @@ def prefill_sweep(args, dev):
             "chunk_len": clen, "prefixes": (b.lens_pf - clen).tolist(),
             "num_q_heads": Hq, "num_kv_heads": spec.num_kv_heads, "head_dim": D,
             "block_size": spec.block_size, "flops": flops,
-            "us_mean": round(float(d.mean()), 3),
+            "us_mean": round(mean, 3),
+            "us_mean_per_call_events": round(float(d.mean()), 3),
             "us_p10": round(float(np.percentile(d, 10)), 3),
             "us_p90": round(float(np.percentile(d, 90)), 3),
             "tflops": round(tf, 1), "frac_mfma_f16_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
