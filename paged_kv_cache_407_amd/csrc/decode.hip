@@ -100,7 +100,22 @@ __global__ __launch_bounds__((64 * DecodeShape<D, BS>::NW)) void decode_kernel(D
   const int h0 = hg * GH;
   const size_t row0 = (size_t)s * p.num_q_heads + h0;  // first output row
 
+  // The sequence length, the partition's block ids (lane j: entry j, read
+  // from a table index clamped into the row, so the read needs no length)
+  // and the query rows are loaded together, before any of them is used:
+  // one memory latency before the first K/V load instead of three.
+  const int part_blocks = p.part_tokens / BS;
+  const int blk0 = part * part_blocks;  // < max_blocks_per_seq: part < num_parts
+  const int32_t *trow = p.block_tables + (size_t)s * p.max_blocks_per_seq;
+  const int table_id = trow[min(blk0 + lane, p.max_blocks_per_seq - 1)];
   const int L = p.seq_lens[s];
+  const int col = lane % LPR;   // 16-byte column within a token row
+  const int rrow = lane / LPR;  // token row within one wave-wide load
+  h8_t qv[GH];
+#pragma unroll
+  for (int g = 0; g < GH; ++g)
+    qv[g] = as_h8(ld16(p.q + (row0 + g) * D + col * 8));
+
   if (!(L >= 1 && L <= p.max_seq_len && L <= p.max_blocks_per_seq * BS)) {
     if (part == 0)
       for (int i = threadIdx.x; i < GH * D; i += blockDim.x)
@@ -111,30 +126,19 @@ __global__ __launch_bounds__((64 * DecodeShape<D, BS>::NW)) void decode_kernel(D
   if (part >= np_row) return;
 
   const int kvh = h0 / p.group;
-  const int part_blocks = p.part_tokens / BS;
   const int nblk = cdiv(L, BS);
-  const int blk0 = part * part_blocks;
   const int blk1 = min(blk0 + part_blocks, nblk);
   // A wave step may overhang the partition's last block; those zero-filled
   // rows must not enter the softmax.
   const int tok_end = min(L, blk1 * BS);
 
-  // The partition's block ids, lane j holding entry j; an id outside the
-  // pool poisons the whole sequence (every wave sees the same slice).
-  const int32_t *trow = p.block_tables + (size_t)s * p.max_blocks_per_seq;
-  int my_blk = 0;
-  if (lane < blk1 - blk0) my_blk = trow[blk0 + lane];
+  // An id outside the pool poisons the whole sequence (every wave sees the
+  // same slice).
+  int my_blk = lane < blk1 - blk0 ? table_id : 0;
   const bool my_bad =
       lane < blk1 - blk0 && (my_blk < 0 || my_blk >= p.num_blocks);
   if (my_bad) my_blk = 0;
   const bool bad = __any(my_bad);
-
-  const int col = lane % LPR;   // 16-byte column within a token row
-  const int rrow = lane / LPR;  // token row within one wave-wide load
-  h8_t qv[GH];
-#pragma unroll
-  for (int g = 0; g < GH; ++g)
-    qv[g] = as_h8(ld16(p.q + (row0 + g) * D + col * 8));
 
   float m[GH], lsum[GH], acc[GH][8];
 #pragma unroll
@@ -302,7 +306,17 @@ __global__ __launch_bounds__(256) void decode_gqa8_kernel(DecodeParams p) {
   const int h0 = hg * GH;
   const size_t row0 = (size_t)s * p.num_q_heads + h0;
 
+  // Length, block ids (from a clamped table index) and query rows are
+  // loaded together, as in decode_kernel.
+  const int part_blocks = p.part_tokens / BS;
+  const int blk0 = part * part_blocks;
+  const int32_t *trow = p.block_tables + (size_t)s * p.max_blocks_per_seq;
+  const int table_id = trow[min(blk0 + lane, p.max_blocks_per_seq - 1)];
   const int L = p.seq_lens[s];
+  static_assert(GH * SLOTS <= 256, "one query slot per thread");
+  const int qi = min((int)threadIdx.x, GH * SLOTS - 1);
+  const uint4 qslot = ld16(p.q + (row0 + qi / SLOTS) * D + 8 * (qi % SLOTS));
+
   if (!(L >= 1 && L <= p.max_seq_len && L <= p.max_blocks_per_seq * BS)) {
     if (part == 0)
       for (int i = threadIdx.x; i < GH * D; i += blockDim.x)
@@ -313,22 +327,17 @@ __global__ __launch_bounds__(256) void decode_gqa8_kernel(DecodeParams p) {
   if (part >= np_row) return;
 
   const int kvh = h0 / p.group;
-  const int part_blocks = p.part_tokens / BS;
   const int nblk = cdiv(L, BS);
-  const int blk0 = part * part_blocks;
   const int blk1 = min(blk0 + part_blocks, nblk);
   const int tok_end = min(L, blk1 * BS);
 
-  const int32_t *trow = p.block_tables + (size_t)s * p.max_blocks_per_seq;
-  int my_blk = 0;
-  if (lane < blk1 - blk0) my_blk = trow[blk0 + lane];
+  int my_blk = lane < blk1 - blk0 ? table_id : 0;
   const bool my_bad =
       lane < blk1 - blk0 && (my_blk < 0 || my_blk >= p.num_blocks);
   if (my_bad) my_blk = 0;
   const bool bad = __any(my_bad);
 
-  for (int i = threadIdx.x; i < GH * SLOTS; i += blockDim.x)
-    sQ[i] = ld16(p.q + (row0 + i / SLOTS) * D + 8 * (i % SLOTS));
+  if ((int)threadIdx.x < GH * SLOTS) sQ[threadIdx.x] = qslot;
   __syncthreads();
 
   // load layout: lane holds 8 dims (slot col) of token rows rrow + RPL*j
