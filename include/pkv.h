@@ -179,6 +179,36 @@ int pkv_paged_attention_prefill(float *out, const void *q,
                                 size_t workspace_bytes, void *stream);
 
 /*
+ * Host-side checks of the preconditions above that the kernels cannot check
+ * without a synchronisation (plain host code; all pointers are host
+ * pointers, read only).  They follow the cache layout of "LLM 推理引擎 …":
+ * §3.2 (a token's place is slot / block_size, slot % block_size, one token
+ * per place), §3.3 (every logical block below seq_len maps to a physical
+ * block of the pool) and §4.3 (a chunk ends its sequence).  Each returns
+ * PKV_OK, or PKV_ERR_INVALID with *bad_index (may be NULL) set to the first
+ * offending entry, or to -1 when the sizes themselves are invalid.
+ *
+ * pkv_validate_slots  : every slot >= 0 lies below num_blocks * block_size
+ *                       and no two rows share one; negative slots are
+ *                       padding.  bad_index = the row (for a shared slot,
+ *                       the later of the two rows).
+ * pkv_validate_tables : 1 <= seq_lens[s] <= max_blocks_per_seq * block_size
+ *                       and the first ceil(seq_lens[s] / block_size) entries
+ *                       of row s lie in [0, num_blocks).  bad_index =
+ *                       s * max_blocks_per_seq + j (j = 0 for a bad length).
+ * pkv_validate_chunks : cu_q_lens[0] = 0, 0 <= chunk_len <= seq_lens[c],
+ *                       cu_q_lens[num_chunks] = total_q_tokens.  bad_index =
+ *                       the chunk (num_chunks for a wrong total).
+ */
+int pkv_validate_slots(const int32_t *slot_mapping, int32_t num_tokens,
+                       int32_t num_blocks, int32_t block_size, int64_t *bad_index);
+int pkv_validate_tables(const int32_t *block_tables, const int32_t *seq_lens,
+                        int32_t num_seqs, int32_t max_blocks_per_seq,
+                        int32_t num_blocks, int32_t block_size, int64_t *bad_index);
+int pkv_validate_chunks(const int32_t *cu_q_lens, const int32_t *seq_lens,
+                        int32_t num_chunks, int32_t total_q_tokens, int64_t *bad_index);
+
+/*
  * Host-side block manager (plain host code, no device calls, not
  * thread-safe): the free list and per-request block tables that produce the
  * block_tables / seq_lens / slot_mapping arguments above ("LLM 推理引擎 …",

@@ -15,6 +15,7 @@ import ctypes
 import math
 from pathlib import Path
 
+import numpy as np
 import torch
 
 _HERE = Path(__file__).resolve().parent
@@ -38,6 +39,9 @@ SIGNATURES = {
                                                    _I32, _I32, _I32, _I32, _I32, _I32, _I32, _F,
                                                    _P, _SZ, _P]),
     "pkv_prefill_workspace_size": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32]),
+    "pkv_validate_slots": (ctypes.c_int, [_P, _I32, _I32, _I32, _P]),
+    "pkv_validate_tables": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _I32, _P]),
+    "pkv_validate_chunks": (ctypes.c_int, [_P, _P, _I32, _I32, _P]),
     "pkv_bm_create": (_P, [_I32, _I32]),
     "pkv_bm_destroy": (None, [_P]),
     "pkv_bm_num_free": (_I32, [_P]),
@@ -266,6 +270,57 @@ def _pools(src_k, src_v, dst_k, dst_v):
     if s != sv or d != dv or s[1:] != d[1:]:
         raise ValueError("pools must share [Hkv, bs, D] and K/V shapes must match")
     return s[0], d[0], s[1], s[2], s[3]
+
+
+def _host_i32(a, name):
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.int32:
+        raise TypeError(f"{name} must be int32, got {a.dtype}")
+    return a
+
+
+def _validated(rc, bad, what):
+    if rc != PKV_OK:
+        raise PkvError(f"{what}: precondition violated at index {bad.value}")
+
+
+def validate_slots(slot_mapping, num_blocks: int, block_size: int) -> None:
+    """Host check of a slot mapping (numpy int32): every slot >= 0 inside the
+    pool and no slot written twice.  Raises PkvError naming the row."""
+    sl = _host_i32(slot_mapping, "slot_mapping").reshape(-1)
+    bad = ctypes.c_int64(-1)
+    rc = load_library().pkv_validate_slots(sl.ctypes.data, sl.shape[0], int(num_blocks),
+                                           int(block_size), ctypes.byref(bad))
+    _validated(rc, bad, "validate_slots")
+
+
+def validate_tables(block_tables, seq_lens, num_blocks: int, block_size: int) -> None:
+    """Host check of block tables [S, MB] and lengths [S] (numpy int32):
+    1 <= L <= MB * block_size and every live entry inside the pool.  Raises
+    PkvError naming the flat table index (s * MB + j)."""
+    t = _host_i32(block_tables, "block_tables")
+    L = _host_i32(seq_lens, "seq_lens").reshape(-1)
+    if t.ndim != 2 or t.shape[0] != L.shape[0]:
+        raise ValueError("block_tables must be [S, MB] with S = len(seq_lens)")
+    bad = ctypes.c_int64(-1)
+    rc = load_library().pkv_validate_tables(t.ctypes.data, L.ctypes.data, L.shape[0],
+                                            t.shape[1], int(num_blocks), int(block_size),
+                                            ctypes.byref(bad))
+    _validated(rc, bad, "validate_tables")
+
+
+def validate_chunks(cu_q_lens, seq_lens, total_q_tokens: int) -> None:
+    """Host check of prefill chunk bounds (numpy int32): cu_q_lens[0] = 0,
+    0 <= chunk_len <= seq_len, last entry = total_q_tokens.  Raises PkvError
+    naming the chunk."""
+    cu = _host_i32(cu_q_lens, "cu_q_lens").reshape(-1)
+    L = _host_i32(seq_lens, "seq_lens").reshape(-1)
+    if cu.shape[0] != L.shape[0] + 1:
+        raise ValueError("cu_q_lens must have len(seq_lens) + 1 entries")
+    bad = ctypes.c_int64(-1)
+    rc = load_library().pkv_validate_chunks(cu.ctypes.data, L.ctypes.data, L.shape[0],
+                                            int(total_q_tokens), ctypes.byref(bad))
+    _validated(rc, bad, "validate_chunks")
 
 
 def copy_blocks(src_k, src_v, dst_k, dst_v, src_blocks, dst_blocks, stream=None):
