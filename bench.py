@@ -744,43 +744,74 @@ def serve_bench(args, dev):
 
 def cpu_baseline(b: W.Batch, kv_bytes: int, budget_s: float) -> dict:
     """Times the CPU oracle (append + decode [+ prefill]) on a bounded sample
-    of the same batch; the rate is scaled to KV GB/s of the full batch."""
+    of the same batch's rows, with all host threads and with one; the rate
+    is scaled to KV GB/s of the full batch."""
     import oracle
     orc = oracle.get()
     cores = int(os.environ.get("OMP_NUM_THREADS") or len(os.sched_getaffinity(0)))
-    S = b.num_dec
-    Hq = b.spec.num_q_heads
-    # estimate: ~50 M fp64 multiply-adds per second per thread
-    macs = int(b.lens_dec.astype(np.int64).sum()) * Hq * b.spec.head_dim * 2 if S else 0
-    est = macs / (5e7 * cores)
-    frac = 1.0
-    rows = None
-    if est > budget_s:
-        frac = budget_s / est
-        n = max(1, int(S * Hq * frac))
-        rows = np.sort(np.random.default_rng(0).choice(S * Hq, n, replace=False))
-        frac = n / (S * Hq)
-    t0 = time.perf_counter()
-    kc, vc = orc.kv_append(b.new_k, b.new_v, b.k_cache, b.v_cache, b.slot_mapping)
-    t_app = time.perf_counter() - t0
-    reps, t_dec = 0, 0.0
-    while True:
-        t0 = time.perf_counter()
+    S, Hq, D = b.num_dec, b.spec.num_q_heads, b.spec.head_dim
+    T = b.q_pf.shape[0] if b.num_pf else 0
+    # work estimate: ~50 M fp64 multiply-adds per second per thread
+    macs = int(b.lens_dec.astype(np.int64).sum()) * Hq * D * 2 if S else 0
+    if b.num_pf:
+        macs += W.prefill_flops(b) // 2
+
+    def sample(fraction, seed):
+        """(decode rows, prefill rows, the fraction actually taken)."""
+        if fraction >= 1.0:
+            return None, None, 1.0
+        rng = np.random.default_rng(seed)
+        drows = prows = None
+        taken = 1.0
         if S:
-            orc.decode(b.q_dec, kc, vc, b.tables_dec, b.lens_dec, b.scale, rows=rows)
-        if b.num_pf:
-            orc.prefill(b.q_pf, b.cu_q_lens, kc, vc, b.tables_pf, b.lens_pf, b.scale)
-        t_dec += time.perf_counter() - t0
-        reps += 1
-        if t_dec >= budget_s or reps >= 20 or (frac < 1.0):
-            break
-    step = t_app + (t_dec / reps) / frac
-    sample = (f"{reps} run(s) of oracle decode over {'all' if rows is None else len(rows)} of "
-              f"{S * Hq} (sequence, head) rows, plus one kv append; time scaled to the "
-              f"whole batch")
+            n = max(1, int(S * Hq * fraction))
+            drows = np.sort(rng.choice(S * Hq, n, replace=False))
+            taken = n / (S * Hq)
+        if T:
+            n = max(1, int(T * Hq * fraction))
+            prows = np.sort(rng.choice(T * Hq, n, replace=False))
+            if not S:
+                taken = n / (T * Hq)
+        return drows, prows, taken
+
+    def run(threads, budget, seed, max_reps):
+        orc.set_threads(threads)
+        try:
+            drows, prows, frac = sample(min(1.0, budget / max(macs / (5e7 * threads), 1e-9)),
+                                        seed)
+            t0 = time.perf_counter()
+            kc, vc = orc.kv_append(b.new_k, b.new_v, b.k_cache, b.v_cache, b.slot_mapping)
+            t_app = time.perf_counter() - t0
+            reps, t = 0, 0.0
+            while True:
+                t0 = time.perf_counter()
+                if S:
+                    orc.decode(b.q_dec, kc, vc, b.tables_dec, b.lens_dec, b.scale, rows=drows)
+                if T:
+                    orc.prefill(b.q_pf, b.cu_q_lens, kc, vc, b.tables_pf, b.lens_pf, b.scale,
+                                rows=prows)
+                t += time.perf_counter() - t0
+                reps += 1
+                if t >= budget or reps >= max_reps or frac < 1.0:
+                    break
+        finally:
+            orc.set_threads(0)
+        return t_app + (t / reps) / frac, reps, frac
+
+    step, reps, frac = run(cores, budget_s, 0, 20)
+    step1, _, frac1 = run(1, budget_s / 3, 1, 1)
+    what = "decode" + (" and prefill" if T else "")
     return {"value": round(kv_bytes / step / 1e9, 4), "unit": "GB/s", "cores": cores,
-            "kind": "oracle", "sample": sample, "step_s": round(step, 4),
-            "cpu": _cpu_model()}
+            "kind": "oracle",
+            "sample": f"{reps} run(s) of the oracle's {what} over {frac:.2%} of the "
+                      f"(token, head) rows, plus one kv append; time scaled to the whole "
+                      f"batch",
+            "step_s": round(step, 4), "cpu": _cpu_model(),
+            "single_thread": {"value": round(kv_bytes / step1 / 1e9, 4), "cores": 1,
+                              "step_s": round(step1, 4),
+                              "sample": f"one run over {frac1:.2%} of the rows plus one kv "
+                                        f"append, on one thread; time scaled to the whole "
+                                        f"batch"}}
 
 
 def _cpu_model():

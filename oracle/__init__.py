@@ -63,6 +63,8 @@ class Oracle:
         lib.oracle_prefill.restype = ctypes.c_int
         lib.oracle_copy_blocks.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, I32, I32]
         lib.oracle_copy_blocks.restype = ctypes.c_int
+        lib.oracle_set_threads.argtypes = [ctypes.c_int]
+        lib.oracle_set_threads.restype = None
         self.lib = lib
         self.path = path
 
@@ -70,6 +72,10 @@ class Oracle:
     def _check(rc: int, what: str):
         if rc:
             raise OracleError(f"oracle {what}: {_ERRORS.get(rc, rc)}")
+
+    def set_threads(self, n: int):
+        """Threads of the oracle's OpenMP loops; n <= 0 restores the default."""
+        self.lib.oracle_set_threads(int(n))
 
     def half_to_double(self, bits: int) -> float:
         return self.lib.oracle_half_to_double(int(bits) & 0xFFFF)

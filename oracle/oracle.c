@@ -47,9 +47,20 @@
  * 3 duplicate slot; 4 out of memory.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+
+/* Threads of the OpenMP loops below (for timing the oracle on one core);
+ * n <= 0 restores the count the process started with.  Not arithmetic. */
+void oracle_set_threads(int n)
+{
+    static int initial = 0;
+    if (!initial)
+        initial = omp_get_max_threads();
+    omp_set_num_threads(n > 0 ? n : initial);
+}
 
 /* IEEE 754 binary16 -> double, from the format's definition: 1 sign bit,
  * 5 exponent bits (bias 15), 10 fraction bits; exponent 0 encodes zero and
