@@ -182,7 +182,15 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p,
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
     o[dt][0] = o[dt][1] = f4_t{0.f, 0.f, 0.f, 0.f};
-  float m[2] = {kMaxFloor, kMaxFloor}, l[2] = {0.f, 0.f};
+  float m[2] = {kMaxFloor, kMaxFloor};
+  // Row sums of the softmax weights come out of the matrix pipe: an all-ones
+  // V^T block beside the DT blocks of PV gives sum_k P^T[k][q] in every row
+  // of its accumulator, in the lanes that hold column q (no vector adds, no
+  // cross-lane sum at the end).
+  f4_t lacc[2] = {f4_t{0.f, 0.f, 0.f, 0.f}, f4_t{0.f, 0.f, 0.f, 0.f}};
+  h8_t ones;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) ones[j] = (_Float16)1.f;
 
   if (tid == 0) sBad = 0;
   // Prologue, ordered so that only two memory latencies are exposed: the
@@ -250,12 +258,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p,
       }
 
       // lane holds keys kbase + 32*(mm/2) + 8g + 4*(mm%2) + r of column lc
-      const bool diag = kbase + BN - 1 > P + wq0;
-      h8_t pb[2][2];
+      if (kbase + BN - 1 > P + wq0) {
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        // raw scores; the scale (> 0) is applied inside the exponent
-        if (diag) {
+        for (int qb = 0; qb < 2; ++qb) {
           const int qpos = P + wq0 + 16 * qb + lc;
 #pragma unroll
           for (int mm = 0; mm < 4; ++mm)
@@ -265,38 +270,46 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p,
               if (kpos > qpos) st[mm][qb][r] = -INFINITY;
             }
         }
-        // the lane's 16 scores of this row, two at a time into a 3-way max
+      }
+      // raw scores; the scale (> 0) is applied inside the exponent.  The
+      // lane's 16 scores of each row, two at a time into a 3-way max.
+      float tm[2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
         float tmax = st[0][qb][0];
 #pragma unroll
         for (int i = 1; i < 15; i += 2)
           tmax = vmax3(tmax, st[i >> 2][qb][i & 3], st[(i + 1) >> 2][qb][(i + 1) & 3]);
-        tmax = max_over_rows(vmax(tmax, st[3][qb][3]));
-        // Lazy rescaling: the running maximum m only moves when some row's
-        // maximum exceeds it by more than 2^8, so weights stay below 256
-        // (exact enough in fp16) and the O rescale is rare.  m starts at a
-        // finite floor, so exp2(-inf) = 0 removes masked keys also in rows
-        // that have not met a visible key yet.
-        const float tm = tmax * p.scale_log2e;
-        if (__any(tm > m[qb] + kLazyRescale)) {
-          const float mnew = fmaxf(m[qb], tm);
+        tm[qb] = max_over_rows(vmax(tmax, st[3][qb][3])) * p.scale_log2e;
+      }
+      // Lazy rescaling: the running maximum m only moves when some row's
+      // maximum exceeds it by more than 2^8, so weights stay below 256
+      // (exact enough in fp16) and the O rescale is rare; one branch serves
+      // both query blocks.  m starts at a finite floor, so exp2(-inf) = 0
+      // removes masked keys also in rows that have not met a visible key yet.
+      if (__any(tm[0] > m[0] + kLazyRescale || tm[1] > m[1] + kLazyRescale)) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          const float mnew = fmaxf(m[qb], tm[qb]);
           const float alpha = fast_exp2(m[qb] - mnew);
           m[qb] = mnew;
-          l[qb] *= alpha;
+          lacc[qb] *= alpha;
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) o[dt][qb] *= alpha;
         }
+      }
+      h8_t pb[2][2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
         const float nm = -m[qb];
-        float psum = 0.f;
 #pragma unroll
         for (int mm = 0; mm < 4; ++mm) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const float e = fast_exp2(fmaf(st[mm][qb][r], p.scale_log2e, nm));
-            psum += e;
             pb[mm >> 1][qb][4 * (mm & 1) + r] = (_Float16)e;
           }
         }
-        l[qb] += psum;
       }
       // O^T[d][q] += sum_k V^T[d][k] P^T[k][q]; slot j of lane group g is key
       // 32ks + 8g + j on both sides.  Step i = (ks, dt); its V^T fragment
@@ -315,6 +328,11 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p,
         o[i % DT][0] = mfma16x16x32(a, pb[i / DT][0], o[i % DT][0]);
         o[i % DT][1] = mfma16x16x32(a, pb[i / DT][1], o[i % DT][1]);
       }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        lacc[0] = mfma16x16x32(ones, pb[ks][0], lacc[0]);
+        lacc[1] = mfma16x16x32(ones, pb[ks][1], lacc[1]);
+      }
     }
     if (kt + 1 < t_hi) store(buf ^ 1);
     __syncthreads();
@@ -327,7 +345,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p,
                          __builtin_nanf("")};
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const float lt = sum_over_rows(l[qb]);
+    const float lt = lacc[qb][0];  // every row of the ones block holds the sum
     const int qr = wq0 + 16 * qb + lc;
     if (qr >= qlen) continue;
     const size_t row = (size_t)(q_begin + qr) * Hq + h;
