@@ -336,20 +336,23 @@ int pkv_sched_step(pkv_scheduler *s, int32_t max_blocks_per_seq, int32_t pad_blo
  * Native step executor over a scheduler (continuous batching, "LLM 推理引擎
  * …", §2.2: each forward step runs the recomposed batch, prefill chunks and
  * decode rows together).  pkv_server_create allocates, once: two pinned
- * staging buffers and two device copies of a step's plan, and the decode
- * workspace for max_batch_size rows of up to max_seq_len tokens.  max_batch_size,
+ * staging buffers and two device copies of a step's plan, the attention
+ * workspace for max_batch_size rows of up to max_seq_len tokens, and a
+ * copy stream of its own (default priority).  max_batch_size,
  * max_num_tokens and max_seq_len must equal the scheduler's; the pools are
  * the caller's device buffers ([num_blocks][Hkv][bs][D] fp16, bs = the
  * block manager's).  NULL on invalid arguments or a failed allocation.
  *   pkv_server_plan: runs pkv_sched_step into the staging buffer not used
  *     by the previous step (after waiting for its copy of two steps ago)
- *     and enqueues its host-to-device copy on `stream`.
+ *     and enqueues its host-to-device copy on the copy stream, after the
+ *     kernels of the step that last read that device buffer; `stream` is
+ *     not used.
  *   pkv_server_plan_arrays: host views of the last plan's request ids,
  *     cu_q_lens, prefill_lens, decode_lens, finished and preempted ids
  *     (valid until the next plan), for the caller to produce the step's rows.
- *   pkv_server_execute: enqueues on `stream` the kv append of the plan's
- *     new rows, then the prefill of its chunks and the decode of its decode
- *     rows.  new_k / new_v [num_new_tokens][Hkv][D] and q
+ *   pkv_server_execute: makes `stream` wait for the plan's copy, then
+ *     enqueues on it the kv append of the plan's new rows, the prefill of
+ *     its chunks and the decode of its decode rows.  new_k / new_v [num_new_tokens][Hkv][D] and q
  *     [num_new_tokens][Hq][D] fp16, device, in slot_mapping order (the
  *     chunks' tokens, then one row per decode request); out_prefill
  *     [num_prefill_tokens][Hq][D] and out_decode [num_decode][Hq][D] fp32,

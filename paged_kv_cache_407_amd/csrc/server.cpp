@@ -6,10 +6,13 @@
 //
 // pkv_server_plan: waits until the staging buffer it is about to reuse has
 // been copied (two buffers in turn), runs pkv_sched_step into it, and
-// enqueues its host-to-device copy on the stream.
-// pkv_server_execute: enqueues pkv_kv_append of the step's new rows, the
-// prefill of its chunks and the decode of its decode rows, reading the
-// plan from the device copy.
+// enqueues its host-to-device copy on the executor's own copy stream, after
+// the kernels of the step that last read that device buffer.
+// pkv_server_execute: makes the caller's stream wait for the plan's copy,
+// then enqueues pkv_kv_append of the step's new rows, the prefill of its
+// chunks and the decode of its decode rows, reading the plan from the
+// device copy.  The copy of the next step's plan thus runs beside this
+// step's kernels instead of between two steps.
 // Staging and the attention workspace are allocated once, when the server
 // is created; the caller owns the pools, the new rows and the outputs.
 #include <hip/hip_runtime.h>
@@ -30,8 +33,11 @@ struct pkv_server {
   size_t o_cu, o_pt, o_pl, o_dt, o_dl, o_sl, n_ints;
   int32_t *host[2] = {nullptr, nullptr};
   int32_t *dev[2] = {nullptr, nullptr};
-  hipEvent_t copied[2] = {nullptr, nullptr};
+  hipEvent_t copied[2] = {nullptr, nullptr};   // plan i is on the device
+  hipEvent_t consumed[2] = {nullptr, nullptr}; // the kernels reading dev[i] are done
   bool pending[2] = {false, false};
+  bool in_use[2] = {false, false};             // consumed[i] was recorded
+  hipStream_t copy_stream = nullptr;
   int64_t *ids = nullptr;  // [4][B]: prefill, decode, finished, preempted
   void *ws = nullptr;
   size_t ws_bytes = 0;
@@ -42,10 +48,16 @@ struct pkv_server {
   void release() {
     for (int i = 0; i < 2; ++i) {
       if (copied[i]) (void)hipEventSynchronize(copied[i]);
+      if (consumed[i]) (void)hipEventSynchronize(consumed[i]);
+    }
+    if (copy_stream) (void)hipStreamSynchronize(copy_stream);
+    for (int i = 0; i < 2; ++i) {
       if (host[i]) (void)hipHostFree(host[i]);
       if (dev[i]) (void)hipFree(dev[i]);
       if (copied[i]) (void)hipEventDestroy(copied[i]);
+      if (consumed[i]) (void)hipEventDestroy(consumed[i]);
     }
+    if (copy_stream) (void)hipStreamDestroy(copy_stream);
     if (ws) (void)hipFree(ws);
     delete[] ids;
   }
@@ -104,7 +116,10 @@ pkv_server *pkv_server_create(pkv_scheduler *sched, pkv_block_manager *bm, void 
     ok = hipHostMalloc((void **)&s->host[i], s->n_ints * 4, hipHostMallocDefault) ==
              hipSuccess &&
          hipMalloc((void **)&s->dev[i], s->n_ints * 4) == hipSuccess &&
-         hipEventCreateWithFlags(&s->copied[i], hipEventDisableTiming) == hipSuccess;
+         hipEventCreateWithFlags(&s->copied[i], hipEventDisableTiming) == hipSuccess &&
+         hipEventCreateWithFlags(&s->consumed[i], hipEventDisableTiming) == hipSuccess;
+  // default priority, like every stream here
+  ok = ok && hipStreamCreateWithFlags(&s->copy_stream, hipStreamNonBlocking) == hipSuccess;
   ok = ok && (s->ws_bytes == 0 || hipMalloc(&s->ws, s->ws_bytes) == hipSuccess);
   if (!ok) {
     (void)hipGetLastError();
@@ -136,9 +151,11 @@ int pkv_server_plan(pkv_server *s, pkv_step_plan *plan, void *stream) {
   s->planned = true;
   *plan = s->plan;
   if (s->plan.num_new_tokens == 0) return PKV_OK;
-  hipStream_t st = (hipStream_t)stream;
-  if (hipMemcpyAsync(s->dev[i], h, s->n_ints * 4, hipMemcpyHostToDevice, st) != hipSuccess ||
-      hipEventRecord(s->copied[i], st) != hipSuccess)
+  (void)stream;  // the copy runs on the executor's copy stream
+  hipStream_t cs = s->copy_stream;
+  if ((s->in_use[i] && hipStreamWaitEvent(cs, s->consumed[i], 0) != hipSuccess) ||
+      hipMemcpyAsync(s->dev[i], h, s->n_ints * 4, hipMemcpyHostToDevice, cs) != hipSuccess ||
+      hipEventRecord(s->copied[i], cs) != hipSuccess)
     return PKV_ERR_HIP;
   s->pending[i] = true;
   return PKV_OK;
@@ -170,6 +187,8 @@ int pkv_server_execute(pkv_server *s, const void *new_k, const void *new_v, cons
     return PKV_ERR_INVALID;
   const int32_t *h = s->host[s->cur];
   const int32_t *d = s->dev[s->cur];
+  hipStream_t st = (hipStream_t)stream;
+  if (hipStreamWaitEvent(st, s->copied[s->cur], 0) != hipSuccess) return PKV_ERR_HIP;
   int rc = pkv_kv_append(new_k, new_v, s->k_cache, s->v_cache, d + s->o_sl,
                          p.num_new_tokens, s->Hkv, s->D, s->bs, s->NB, stream);
   if (rc != PKV_OK) return rc;
@@ -197,6 +216,9 @@ int pkv_server_execute(pkv_server *s, const void *new_k, const void *new_v, cons
         s->MB, max_len, s->scale, 0, s->ws, s->ws_bytes, stream);
     if (rc != PKV_OK) return rc;
   }
+  // the next copy into this device buffer waits for these kernels
+  if (hipEventRecord(s->consumed[s->cur], st) != hipSuccess) return PKV_ERR_HIP;
+  s->in_use[s->cur] = true;
   return PKV_OK;
 }
 
