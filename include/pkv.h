@@ -153,7 +153,7 @@ int pkv_paged_attention_decode(float *out, const void *q, const void *k_cache,
  *                  exceeds it gets NaN rows
  *   scale        : as for the decode
  *   workspace    : device scratch of at least pkv_prefill_workspace_size()
- *                  bytes, 256-byte aligned (may be NULL when that size is 0).
+ *                  bytes, 16-byte aligned (may be NULL when that size is 0).
  *                  When the grid of query tiles is small, a query tile's key
  *                  range is cut into parts run by different workgroups; the
  *                  parts leave partial outputs here and a second kernel

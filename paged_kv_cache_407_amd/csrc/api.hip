@@ -331,7 +331,7 @@ int pkv_paged_attention_prefill(float *out, const void *q,
   p.split_tiles = sp.tiles;
   p.ws_o = p.ws_m = p.ws_l = nullptr;
   if (sp.parts > 1) {
-    if (!workspace || workspace_bytes < sp.bytes || ((uintptr_t)workspace & 255u))
+    if (!workspace || workspace_bytes < sp.bytes || !aligned16(workspace))
       return PKV_ERR_INVALID;
     char *w = (char *)workspace;
     p.ws_o = (float *)(w + sp.o_off);
