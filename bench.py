@@ -60,6 +60,10 @@ def parse():
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough for cold caches")
     ap.add_argument("--partition-size", type=int, default=0)
     ap.add_argument("--no-graph", action="store_true", help="eager launches")
+    ap.add_argument("--no-order", action="store_true",
+                    help="dispatch decode sequences in batch order (default: the host "
+                         "passes a longest-first order, as a serving loop that knows its "
+                         "lengths does)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -329,10 +333,15 @@ def main():
     def do_append(rep):
         pkv.kv_append(rep["nk"], rep["nv"], rep["kc"], rep["vc"], slots)
 
+    # the dispatch order, from the host's copy of the lengths (planning work,
+    # outside the timed region)
+    order = None if (args.no_order or not S) else pkv.longest_first(b.lens_dec)
+
     def do_decode(rep):
         pkv.paged_attention_decode(rep["q"], rep["kc"], rep["vc"], tab, lens,
                                    max_seq_len=max_len, scale=b.scale, out=rep["out"],
-                                   workspace=rep["ws"], partition_size=args.partition_size)
+                                   workspace=rep["ws"], partition_size=args.partition_size,
+                                   seq_order=order)
 
     def do_prefill(rep):
         pkv.paged_attention_prefill(rep["qp"], cu, rep["kc"], rep["vc"], tabp, lensp,
@@ -430,6 +439,7 @@ def main():
             "block_size": spec.block_size, "seq_lens_total": int(b.lens_dec.sum()) if S else 0,
             "max_seq_len": max_len, "partition_size": part, "replicas": R,
             "graph": graphs is not None,
+            "dispatch_order": "batch" if order is None else "longest_first",
             "steps_per_graph": R if graphs is not None else 0,
         },
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
@@ -504,6 +514,7 @@ def block_size_sweep(args, dev):
             return torch.from_numpy(a).to(dev)
         nk, nv, slots = to_dev(b.new_k), to_dev(b.new_v), to_dev(b.slot_mapping)
         tab, lens, q = to_dev(b.tables_dec), to_dev(b.lens_dec), to_dev(b.q_dec)
+        order = None if args.no_order else pkv.longest_first(b.lens_dec)
         reps = []
         for r in range(R):
             kc, vc = to_dev(b.k_cache), to_dev(b.v_cache)
@@ -515,7 +526,8 @@ def block_size_sweep(args, dev):
             kc, vc, out, ws = rep
             pkv.paged_attention_decode(q, kc, vc, tab, lens, max_seq_len=max_len,
                                        scale=b.scale, out=out, workspace=ws,
-                                       partition_size=args.partition_size)
+                                       partition_size=args.partition_size,
+                                       seq_order=order)
         for i in range(args.warmup):
             call(reps[i % R])
         n = max(args.steps, 20)

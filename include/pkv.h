@@ -111,6 +111,13 @@ int32_t pkv_decode_partition_size(int32_t num_seqs, int32_t num_q_heads,
  *                  0 = library's choice.  Partitions are merged with the
  *                  log-sum-exp identity of the running max / sum recurrence
  *                  (a second kernel, enqueued by the same call).
+ *   seq_order    : host, [num_seqs] int32, may be NULL: the order in which
+ *                  the sequences' workgroups are dispatched (a permutation
+ *                  of 0 .. num_seqs-1, else PKV_ERR_INVALID).  A hint only:
+ *                  outputs are identical for every order.  Longest first
+ *                  keeps long sequences from running on alone at the end.
+ *                  Used for batches of at most 256 sequences (it travels in
+ *                  the kernel arguments), ignored above.
  *   workspace    : device, at least pkv_decode_workspace_size(...) bytes,
  *                  16-byte aligned, owned by the caller (may be NULL when
  *                  that size is 0).  Its contents on entry do not matter and
@@ -127,8 +134,9 @@ int pkv_paged_attention_decode(float *out, const void *q, const void *k_cache,
                                int32_t head_dim, int32_t block_size,
                                int32_t num_blocks, int32_t max_blocks_per_seq,
                                int32_t max_seq_len, float scale,
-                               int32_t partition_size, void *workspace,
-                               size_t workspace_bytes, void *stream);
+                               int32_t partition_size, const int32_t *seq_order,
+                               void *workspace, size_t workspace_bytes,
+                               void *stream);
 
 /*
  * Paged attention prefill of causal chunks whose prefix already sits in

@@ -34,7 +34,8 @@ SIGNATURES = {
     "pkv_decode_workspace_size": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
     "pkv_decode_partition_size": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
     "pkv_paged_attention_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32,
-                                                  _I32, _I32, _I32, _I32, _F, _I32, _P, _SZ, _P]),
+                                                  _I32, _I32, _I32, _I32, _F, _I32, _P, _P, _SZ,
+                                                  _P]),
     "pkv_paged_attention_prefill": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32,
                                                    _I32, _I32, _I32, _I32, _I32, _I32, _I32, _F,
                                                    _P, _SZ, _P]),
@@ -165,12 +166,14 @@ def decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_s
 
 def paged_attention_decode(q, k_cache, v_cache, block_tables, seq_lens, *, max_seq_len: int,
                            scale: float | None = None, out=None, workspace=None,
-                           partition_size: int = 0, stream=None):
+                           partition_size: int = 0, seq_order=None, stream=None):
     """out[S, Hq, D] (float32) of one query token per sequence.
 
     ``workspace`` (uint8, at least ``decode_workspace_size(...)`` bytes) holds
     the split partials; one buffer serves any number of calls on the same
-    stream.  Without it a buffer is allocated for the call."""
+    stream.  Without it a buffer is allocated for the call.  ``seq_order``
+    (host int32 permutation of the batch, optional) is the dispatch order,
+    e.g. ``longest_first(host_lengths)``; outputs do not depend on it."""
     NB, Hkv, bs, D = _cache_shape(k_cache, v_cache)
     _dev(q, "q", torch.float16, 3)
     _dev(block_tables, "block_tables", torch.int32, 2)
@@ -193,12 +196,26 @@ def paged_attention_decode(q, k_cache, v_cache, block_tables, seq_lens, *, max_s
     if workspace is not None:
         _dev(workspace, "workspace", torch.uint8, 1)
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
+    order_ptr = None
+    if seq_order is not None:
+        seq_order = _host_i32(seq_order, "seq_order").reshape(-1)
+        if seq_order.shape[0] != S:
+            raise ValueError("seq_order must have one entry per sequence")
+        order_ptr = seq_order.ctypes.data
     rc = load_library().pkv_paged_attention_decode(
         out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
         block_tables.data_ptr(), seq_lens.data_ptr(), S, Hq, Hkv, D, bs, NB, MB,
-        int(max_seq_len), float(scale), int(partition_size), ws_ptr, ws_bytes, _stream(stream))
+        int(max_seq_len), float(scale), int(partition_size), order_ptr, ws_ptr, ws_bytes,
+        _stream(stream))
     _check(rc, "paged_attention_decode")
     return out
+
+
+def longest_first(seq_lens) -> np.ndarray:
+    """The dispatch order that starts the longest sequences first (host
+    int32, ties in batch order) for ``paged_attention_decode(seq_order=)``."""
+    L = np.asarray(seq_lens).reshape(-1)
+    return np.argsort(-L.astype(np.int64), kind="stable").astype(np.int32)
 
 
 def prefill_workspace_size(num_chunks, total_q_tokens, max_q_len, num_q_heads, head_dim,

@@ -225,8 +225,9 @@ int pkv_paged_attention_decode(float *out, const void *q, const void *k_cache,
                                int32_t head_dim, int32_t block_size,
                                int32_t num_blocks, int32_t max_blocks_per_seq,
                                int32_t max_seq_len, float scale,
-                               int32_t partition_size, void *workspace,
-                               size_t workspace_bytes, void *stream) {
+                               int32_t partition_size, const int32_t *seq_order,
+                               void *workspace, size_t workspace_bytes,
+                               void *stream) {
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
       block_size <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 ||
       max_seq_len <= 0 || num_q_heads % num_kv_heads || !isfinite(scale) || !(scale > 0.f))
@@ -270,6 +271,19 @@ int pkv_paged_attention_decode(float *out, const void *q, const void *k_cache,
   p.part_tokens = part;
   p.num_parts = w.num_parts;
   p.scale_log2e = scale * kLog2e;
+  // the dispatch order: a permutation of the batch, carried in the kernel
+  // arguments (ignored for batches above kMaxOrderSeqs)
+  p.has_order = 0;
+  if (seq_order && num_seqs <= kMaxOrderSeqs) {
+    bool seen[kMaxOrderSeqs] = {};
+    for (int32_t i = 0; i < num_seqs; ++i) {
+      const int32_t v = seq_order[i];
+      if (v < 0 || v >= num_seqs || seen[v]) return PKV_ERR_INVALID;
+      seen[v] = true;
+      p.order[i] = (int16_t)v;
+    }
+    p.has_order = 1;
+  }
   return hip_status(launch_decode(p, head_dim, block_size, (hipStream_t)stream));
 }
 

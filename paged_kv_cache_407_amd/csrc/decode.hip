@@ -95,7 +95,8 @@ __global__ __launch_bounds__((64 * DecodeShape<D, BS>::NW)) void decode_kernel(D
   int idx = blockIdx.x;
   const int hg = idx % HG;
   idx /= HG;
-  const int s = idx % p.num_seqs;
+  const int slot = idx % p.num_seqs;
+  const int s = p.has_order ? p.order[slot] : slot;
   const int part = idx / p.num_seqs;
   const int h0 = hg * GH;
   const size_t row0 = (size_t)s * p.num_q_heads + h0;  // first output row
@@ -301,7 +302,8 @@ __global__ __launch_bounds__(256) void decode_gqa8_kernel(DecodeParams p) {
   int idx = blockIdx.x;
   const int hg = idx % HG;
   idx /= HG;
-  const int s = idx % p.num_seqs;
+  const int slot = idx % p.num_seqs;
+  const int s = p.has_order ? p.order[slot] : slot;
   const int part = idx / p.num_seqs;
   const int h0 = hg * GH;
   const size_t row0 = (size_t)s * p.num_q_heads + h0;

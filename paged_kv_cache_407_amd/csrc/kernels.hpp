@@ -16,6 +16,9 @@ struct AppendParams {
   int64_t num_slots;
 };
 
+// Longest batch whose dispatch order travels in the kernel arguments.
+constexpr int kMaxOrderSeqs = 256;
+
 struct DecodeParams {
   float *out;                   // [S][Hq][D]
   const _Float16 *q;            // [S][Hq][D]
@@ -30,6 +33,10 @@ struct DecodeParams {
   int32_t num_blocks, max_blocks_per_seq, max_seq_len;
   int32_t part_tokens, num_parts;
   float scale_log2e;
+  // Dispatch order (kernel arguments, read with scalar loads): grid slot i
+  // runs sequence order[i] when has_order; results do not depend on it.
+  int32_t has_order;
+  int16_t order[kMaxOrderSeqs];
 };
 
 struct PrefillParams {

@@ -20,6 +20,7 @@
 
 #include <algorithm>
 #include <new>
+#include <vector>
 
 #include "pkv.h"
 
@@ -41,6 +42,7 @@ struct pkv_server {
   int64_t *ids = nullptr;  // [4][B]: prefill, decode, finished, preempted
   void *ws = nullptr;
   size_t ws_bytes = 0;
+  std::vector<int32_t> order;  // decode dispatch order of the current step
   int cur = 1;  // staging buffer of the last plan
   pkv_step_plan plan{};
   bool planned = false;
@@ -210,10 +212,16 @@ int pkv_server_execute(pkv_server *s, const void *new_k, const void *new_v, cons
   if (p.num_decode) {
     int32_t max_len = 0;
     for (int32_t k = 0; k < p.num_decode; ++k) max_len = std::max(max_len, h[s->o_dl + k]);
+    // dispatch the longest decode rows first (the lengths are on the host)
+    s->order.resize(p.num_decode);
+    for (int32_t k = 0; k < p.num_decode; ++k) s->order[k] = k;
+    const int32_t *dl = h + s->o_dl;
+    std::stable_sort(s->order.begin(), s->order.end(),
+                     [dl](int32_t a, int32_t b) { return dl[a] > dl[b]; });
     rc = pkv_paged_attention_decode(
         out_decode, (const char *)q + (size_t)p.num_prefill_tokens * qrow, s->k_cache,
         s->v_cache, d + s->o_dt, d + s->o_dl, p.num_decode, s->Hq, s->Hkv, s->D, s->bs, s->NB,
-        s->MB, max_len, s->scale, 0, s->ws, s->ws_bytes, stream);
+        s->MB, max_len, s->scale, 0, s->order.data(), s->ws, s->ws_bytes, stream);
     if (rc != PKV_OK) return rc;
   }
   // the next copy into this device buffer waits for these kernels

@@ -55,14 +55,14 @@ class DevBatch:
         pkv.kv_append(self.new_k, self.new_v, self.k_cache, self.v_cache, self.slots)
 
     def decode(self, partition_size=0, tables=None, lens=None, max_seq_len=None,
-               k_cache=None, v_cache=None):
+               k_cache=None, v_cache=None, seq_order=None):
         return pkv.paged_attention_decode(
             self.q_dec, self.k_cache if k_cache is None else k_cache,
             self.v_cache if v_cache is None else v_cache,
             self.tables_dec if tables is None else tables,
             self.lens_dec if lens is None else lens,
             max_seq_len=max_seq_len or self.max_len_dec, scale=self.b.scale,
-            partition_size=partition_size)
+            partition_size=partition_size, seq_order=seq_order)
 
     def prefill(self, tables=None, k_cache=None, v_cache=None):
         return pkv.paged_attention_prefill(

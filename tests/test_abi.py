@@ -91,19 +91,25 @@ def test_invalid_arguments_are_rejected_on_the_host():
     assert lib.pkv_kv_append(None, None, None, None, None, 0, 2, 64, 16, 8, None) == 0
     dec = lib.pkv_paged_attention_decode
     # Hq not a multiple of Hkv
-    assert dec(P, P, P, P, P, P, 2, 6, 4, 128, 16, 8, 4, 64, 0.1, 0, None, 0, None) == 1
+    assert dec(P, P, P, P, P, P, 2, 6, 4, 128, 16, 8, 4, 64, 0.1, 0, None, None, 0, None) == 1
     # unsupported head_dim / block size
-    assert dec(P, P, P, P, P, P, 2, 4, 4, 96, 16, 8, 4, 64, 0.1, 0, None, 0, None) == 2
-    assert dec(P, P, P, P, P, P, 2, 4, 4, 128, 4, 8, 16, 64, 0.1, 0, None, 0, None) == 2
-    assert dec(P, P, P, P, P, P, 2, 4, 4, 128, 2, 8, 32, 64, 0.1, 0, None, 0, None) == 2
+    assert dec(P, P, P, P, P, P, 2, 4, 4, 96, 16, 8, 4, 64, 0.1, 0, None, None, 0, None) == 2
+    assert dec(P, P, P, P, P, P, 2, 4, 4, 128, 4, 8, 16, 64, 0.1, 0, None, None, 0, None) == 2
+    assert dec(P, P, P, P, P, P, 2, 4, 4, 128, 2, 8, 32, 64, 0.1, 0, None, None, 0, None) == 2
     # max_seq_len beyond the table
-    assert dec(P, P, P, P, P, P, 2, 4, 4, 128, 16, 8, 4, 65, 0.1, 0, None, 0, None) == 1
+    assert dec(P, P, P, P, P, P, 2, 4, 4, 128, 16, 8, 4, 65, 0.1, 0, None, None, 0, None) == 1
     # split needed but no workspace
-    assert dec(P, P, P, P, P, P, 2, 4, 4, 128, 16, 8, 64, 1024, 0.1, 0, None, 0, None) == 1
+    assert dec(P, P, P, P, P, P, 2, 4, 4, 128, 16, 8, 64, 1024, 0.1, 0, None, None, 0, None) == 1
     # non-finite or non-positive scale
-    assert dec(P, P, P, P, P, P, 2, 4, 4, 128, 16, 8, 4, 64, float("nan"), 0, None, 0, None) == 1
-    assert dec(P, P, P, P, P, P, 2, 4, 4, 128, 16, 8, 4, 64, 0.0, 0, None, 0, None) == 1
-    assert dec(P, P, P, P, P, P, 2, 4, 4, 128, 16, 8, 4, 64, -0.1, 0, None, 0, None) == 1
+    assert dec(P, P, P, P, P, P, 2, 4, 4, 128, 16, 8, 4, 64, float("nan"), 0, None, None, 0, None) == 1
+    assert dec(P, P, P, P, P, P, 2, 4, 4, 128, 16, 8, 4, 64, 0.0, 0, None, None, 0, None) == 1
+    assert dec(P, P, P, P, P, P, 2, 4, 4, 128, 16, 8, 4, 64, -0.1, 0, None, None, 0, None) == 1
+    # the dispatch order must be a permutation of the batch
+    import numpy as np
+    for bad in ([0, 0], [0, 2], [-1, 1]):
+        order = np.array(bad, np.int32)
+        assert dec(P, P, P, P, P, P, 2, 4, 4, 128, 16, 8, 4, 64, 0.1, 0, order.ctypes.data,
+                   None, 0, None) == 1
     pre = lib.pkv_paged_attention_prefill
     assert pre(P, P, P, P, P, P, P, 1, 8, 8, 4, 3, 128, 16, 8, 4, 64, 0.1, None, 0, None) == 1
     assert pre(P, P, P, P, P, P, P, 1, 8, 8, 4, 4, 80, 16, 8, 4, 64, 0.1, None, 0, None) == 2

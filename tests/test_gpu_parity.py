@@ -199,6 +199,23 @@ def test_decode_split_matches_unsplit():
         assert err <= 1e-6
 
 
+@pytest.mark.parametrize("name", ["llama_decode", "gqa_shared", "tiny"])
+def test_decode_dispatch_order_is_bitwise_neutral(name):
+    # the dispatch order only changes when a sequence runs, never its result
+    say("decode dispatch order", name)
+    b = W.make_batch(name)
+    dev = DevBatch(b)
+    dev.append()
+    base = to_host(dev.decode())
+    orders = [pkv.longest_first(b.lens_dec),
+              np.random.default_rng(3).permutation(b.num_dec).astype(np.int32)]
+    for order in orders:
+        got = to_host(dev.decode(seq_order=order))
+        assert np.array_equal(got.view(np.uint32), base.view(np.uint32))
+    kc, vc = check_append(b, dev)
+    check_decode(b, kc, vc, to_host(dev.decode(seq_order=orders[0])))
+
+
 def test_decode_permutation_invariance_bitwise():
     b = W.make_batch("llama_decode")
     dev = DevBatch(b)
