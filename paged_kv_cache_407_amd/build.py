@@ -33,9 +33,15 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-I", str(ROOT / "include"), "-I", str(CSRC)]
 
 
+# Per-source options.  decode.hip: MFMA accumulators in ordinary VGPRs; the
+# grouped-query decode rescales and stores them with vector ALU code every
+# step, which otherwise copies them between AGPRs and VGPRs around each MFMA.
+SOURCE_FLAGS = {"decode.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: Path, verbose: bool) -> Path:
     obj = BUILD / (src.stem + ".o")
-    cmd = [hipcc(), *FLAGS, "-c", str(src), "-o", str(obj)]
+    cmd = [hipcc(), *FLAGS, *SOURCE_FLAGS.get(src.name, []), "-c", str(src), "-o", str(obj)]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -98,6 +98,11 @@ __device__ __forceinline__ uint4 ld16_nt(const void *p) {
   const u4v_t v = __builtin_nontemporal_load(reinterpret_cast<const u4v_t *>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
 }
+typedef unsigned u2v_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint2 ld8_nt(const void *p) {
+  const u2v_t v = __builtin_nontemporal_load(reinterpret_cast<const u2v_t *>(p));
+  return make_uint2(v.x, v.y);
+}
 __device__ __forceinline__ void st16(void *p, uint4 v) {
   *reinterpret_cast<uint4 *>(p) = v;
 }

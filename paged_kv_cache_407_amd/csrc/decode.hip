@@ -513,6 +513,266 @@ __global__ __launch_bounds__(256) void decode_gqa8_kernel(DecodeParams p) {
   }
 }
 
+// Decode for 8 query heads per KV head on the matrix cores.
+//
+// With 8 query heads sharing every K/V row, the scores of a 32-token step
+// are the product of an [8 x D] query block with D x 32 keys, and the output
+// update is an [8 x 32] weight block times 32 x D values: dense contractions
+// of 8 FLOP per logical K/V byte, past the point where the vector ALUs (no
+// packed fp32) keep up with HBM.  Both run here as v_mfma_f32_16x16x32_f16
+// tiles, the 8 query heads padded to 16 columns with zeros:
+// * S^T (16 tokens x 16 heads) = K_tile (16 x D) . Q^T.  Lane l supplies
+//   K row l%16, dims 32kk + 8(l/16) .. +7 of k-step kk.  K is loaded with
+//   16 lanes per row (whole rows per load instruction, as V) and handed to
+//   the operand layout through a wave-private LDS tile: read straight into
+//   the operand registers, each load instruction would touch 16 rows in
+//   64-byte pieces, which the memory path serves markedly slower.
+// * Lane l then holds the scores of head l%16 for tokens 16i + 4(l/16) + r
+//   (tile i, r < 4).  Those 8 weights, in that order, are exactly the lane's
+//   P^T operand of the next product (contraction index 8(l/16) + j <->
+//   token 16(j/4) + 4(l/16) + j%4), so they move nowhere.
+// * O^T (D x 16 heads) += V^T (D x 32 tokens) . P^T.  Lane l loads the 16
+//   (D = 128) or 8 (D = 64) bytes at dims VD*(l%16) .. of its 8 tokens:
+//   each load instruction reads 4 whole rows.  An 8 x 8 (or 4 x 8) register
+//   transpose turns them into the V^T operands of VD m-tiles, m-tile mt
+//   holding dim VD*(l%16) + mt in row l%16.  Lane l ends with head l%16's
+//   output at the contiguous dims 4VD(l/16) .. 4VD(l/16) + 4VD - 1.
+// * The fp32 weights enter the PV as an fp16 high part and an fp16 low part
+//   (two MFMAs), so the product keeps about 22 bits of each weight, as fp32
+//   accumulation on the vector ALUs would.
+// * Softmax runs in base 2 with a lazily moved running maximum, as in
+//   decode_gqa8_kernel; masked tokens are removed by selection.
+template <int D, int BS>
+__global__ __launch_bounds__(256) void decode_gqa8_mfma_kernel(DecodeParams p) {
+  constexpr int GH = 8, NW = 4;
+  constexpr int TOK = 32;        // tokens per wave step: two 16-row tiles
+  constexpr int CH = TOK / BS;   // blocks per wave step
+  constexpr int KQ = D / 32;     // k-steps of the score product
+  constexpr int VD = D / 16;     // dims per lane of a V row; PV m-tiles
+  constexpr int SLOTS = D / 8;         // 16-byte chunks of a row
+  constexpr int KRPI = kWave / SLOTS;  // K rows per coalesced wave-wide load
+  constexpr int KNI = 16 / KRPI;       // K loads per lane per 16-row tile
+  static_assert(BS == 16 || BS == 32, "16-row tiles inside one block");
+  static_assert(D == 64 || D == 128, "head_dim 64 or 128");
+  __shared__ uint4 sK[NW][TOK * SLOTS];  // wave-private K tile, swizzled
+  __shared__ float s_acc[NW][GH][D];
+  __shared__ float s_m[NW][GH], s_l[NW][GH];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int HG = p.num_q_heads / GH;
+  int idx = blockIdx.x;
+  const int hg = idx % HG;
+  idx /= HG;
+  const int slot = idx % p.num_seqs;
+  const int s = p.has_order ? p.order[slot] : slot;
+  const int part = idx / p.num_seqs;
+  const int h0 = hg * GH;
+  const size_t row0 = (size_t)s * p.num_q_heads + h0;
+  const int hc = lane & 15;  // MFMA column (head) / row (token or dim) index
+  const int g = lane >> 4;   // contraction group of the lane
+
+  // Length, block ids (clamped table index) and query rows are loaded
+  // together, as in decode_kernel.  Q^T operand: head hc, zero for hc >= 8
+  // (the address is clamped into the head group).
+  const int part_blocks = p.part_tokens / BS;
+  const int blk0 = part * part_blocks;
+  const int32_t *trow = p.block_tables + (size_t)s * p.max_blocks_per_seq;
+  const int table_id = trow[min(blk0 + lane, p.max_blocks_per_seq - 1)];
+  const int L = p.seq_lens[s];
+  const uint4 zero = make_uint4(0, 0, 0, 0);
+  h8_t qv[KQ];
+#pragma unroll
+  for (int kk = 0; kk < KQ; ++kk) {
+    const uint4 r = ld16(p.q + (row0 + (hc & 7)) * D + (4 * kk + g) * 8);
+    qv[kk] = as_h8(hc < GH ? r : zero);
+  }
+
+  if (!(L >= 1 && L <= p.max_seq_len && L <= p.max_blocks_per_seq * BS)) {
+    if (part == 0)
+      for (int i = threadIdx.x; i < GH * D; i += blockDim.x)
+        p.out[row0 * D + i] = __builtin_nanf("");
+    return;
+  }
+  const int np_row = cdiv(L, p.part_tokens);
+  if (part >= np_row) return;
+
+  const int kvh = h0 / p.group;
+  const int nblk = cdiv(L, BS);
+  const int blk1 = min(blk0 + part_blocks, nblk);
+  const int tok_end = min(L, blk1 * BS);
+
+  int my_blk = lane < blk1 - blk0 ? table_id : 0;
+  const bool my_bad =
+      lane < blk1 - blk0 && (my_blk < 0 || my_blk >= p.num_blocks);
+  if (my_bad) my_blk = 0;
+  const bool bad = __any(my_bad);
+
+  float m = -INFINITY, lsum = 0.f;  // head hc; the 4 lanes of a head agree on m
+  f4_t acc[VD];
+#pragma unroll
+  for (int mt = 0; mt < VD; ++mt) acc[mt] = f4_t{0.f, 0.f, 0.f, 0.f};
+  const size_t head_elems = (size_t)BS * D;
+  const float cs = p.scale_log2e;
+
+  const int kcol = lane % SLOTS, krow = lane / SLOTS;  // K load layout
+  uint4 *Kw = sK[wave];
+
+  for (int b = blk0 + wave * CH; b < blk1; b += NW * CH) {
+    const int tok0 = b * BS;
+    uint4 kr[2][KNI];       // K: tile i, row q*KRPI + krow, chunk kcol
+    uint32_t vr[2][4][VD / 2];  // V: tile i, token tok0 + 16i + 4g + r
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int bi = (16 * i) / BS;  // block of the tile within the step
+      const bool in = b + bi < blk1;
+      const int phys = __builtin_amdgcn_readlane(my_blk, in ? b + bi - blk0 : 0);
+      const size_t base = ((size_t)phys * p.num_kv_heads + kvh) * head_elems +
+                          (size_t)((16 * i) % BS) * D;
+      const _Float16 *kb = p.k_cache + base + (size_t)krow * D + 8 * kcol;
+      const _Float16 *vb = p.v_cache + base + (size_t)(4 * g) * D + VD * hc;
+#pragma unroll
+      for (int q = 0; q < KNI; ++q)
+        kr[i][q] = in ? ld16_nt(kb + (size_t)q * KRPI * D) : zero;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if constexpr (VD == 8) {
+          const uint4 v = in ? ld16_nt(vb + (size_t)r * D) : zero;
+          vr[i][r][0] = v.x; vr[i][r][1] = v.y; vr[i][r][2] = v.z; vr[i][r][3] = v.w;
+        } else {
+          const uint2 v = in ? ld8_nt(vb + (size_t)r * D) : make_uint2(0, 0);
+          vr[i][r][0] = v.x; vr[i][r][1] = v.y;
+        }
+      }
+    }
+    const bool full = tok0 + TOK <= tok_end;
+    // K through the wave's LDS tile: stored as loaded (16 lanes per row),
+    // read back in the operand layout (4 lanes per row).  Chunk c of row t
+    // sits at slot c ^ (t % SLOTS), so both the stores (one row's chunks per
+    // 8 lanes) and the reads (8 rows' chunk per 8 lanes) hit distinct banks.
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int q = 0; q < KNI; ++q) {
+        const int t = 16 * i + q * KRPI + krow;
+        Kw[t * SLOTS + (kcol ^ (t & (SLOTS - 1)))] = kr[i][q];
+      }
+    uint4 ka[2][KQ];  // A operand: row 16i + hc, dims 32kk + 8g .. +7
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int kk = 0; kk < KQ; ++kk) {
+        const int t = 16 * i + hc;
+        ka[i][kk] = Kw[t * SLOTS + ((4 * kk + g) ^ (t & (SLOTS - 1)))];
+      }
+
+    // scores of both tiles, scaled to base 2; masked tokens -> -inf
+    float x[2][4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      f4_t sc = f4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KQ; ++kk) sc = mfma16x16x32(as_h8(ka[i][kk]), qv[kk], sc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float v = sc[r] * cs;
+        if (!full && tok0 + 16 * i + 4 * g + r >= tok_end) v = -INFINITY;
+        x[i][r] = v;
+        mx = vmax(mx, v);
+      }
+    }
+    // The step's first token is valid, so every head's maximum is finite.
+    mx = max_over_rows(mx);
+    if (__any(mx > m + kLazyRescale)) {
+      const float mnew = vmax(m, mx);
+      const float alpha = fast_exp2(m - mnew);  // 0 while m = -inf
+      m = mnew;
+      lsum *= alpha;
+#pragma unroll
+      for (int mt = 0; mt < VD; ++mt) acc[mt] *= alpha;
+    }
+    // weights: P^T operand, split into fp16 high and low parts
+    h8_t phi, plo;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float e = fast_exp2(x[i][r] - m);
+        lsum += e;
+        const _Float16 hi = (_Float16)e;
+        phi[4 * i + r] = hi;
+        plo[4 * i + r] = (_Float16)(e - (float)hi);
+      }
+    // masked rows carry weight 0 but may hold NaN: select, never multiply
+    if (!full) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (tok0 + 16 * i + 4 * g + r >= tok_end)
+#pragma unroll
+            for (int w = 0; w < VD / 2; ++w) vr[i][r][w] = 0;
+    }
+    // V^T operands: m-tile mt takes half mt of each of the 8 rows
+#pragma unroll
+    for (int mt = 0; mt < VD; ++mt) {
+      uint32_t w4[4];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t a = vr[w / 2][2 * (w % 2)][mt / 2];
+        const uint32_t c = vr[w / 2][2 * (w % 2) + 1][mt / 2];
+        w4[w] = (mt % 2 == 0) ? ((a & 0xffffu) | (c << 16))
+                              : ((a >> 16) | (c & 0xffff0000u));
+      }
+      const h8_t va = __builtin_bit_cast(h8_t, make_uint4(w4[0], w4[1], w4[2], w4[3]));
+      acc[mt] = mfma16x16x32(va, phi, acc[mt]);
+      acc[mt] = mfma16x16x32(va, plo, acc[mt]);
+    }
+  }
+
+  // the 4 lanes of a head hold sums over different tokens
+  lsum = sum_over_rows(lsum);
+  if (hc < GH) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int mt = 0; mt < VD; ++mt)
+        s_acc[wave][hc][VD * (4 * g + r) + mt] = acc[mt][r];
+    if (g == 0) {
+      s_m[wave][hc] = m;
+      s_l[wave][hc] = lsum;
+    }
+  }
+  __syncthreads();
+
+  const bool split = np_row > 1;
+  for (int i = threadIdx.x; i < GH * D; i += blockDim.x) {
+    const int h = i / D, d = i % D;
+    float M = s_m[0][h];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, s_m[w][h]);
+    float o = 0.f, l = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float e = s_m[w][h] > -INFINITY ? fast_exp2(s_m[w][h] - M) : 0.f;
+      o = fmaf(e, s_acc[w][h][d], o);
+      l = fmaf(e, s_l[w][h], l);
+    }
+    if (bad) o = __builtin_nanf("");
+    if (!split) {
+      p.out[(row0 + h) * D + d] = o / l;
+    } else {
+      const size_t pi = (row0 + h) * p.num_parts + part;
+      p.ws_o[pi * D + d] = o;
+      if (d == 0) {
+        p.ws_m[pi] = M;
+        p.ws_l[pi] = l;
+      }
+    }
+  }
+}
+
 template <int D, int BS>
 __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeParams p) {
   const size_t row = blockIdx.x;
@@ -541,8 +801,12 @@ static hipError_t launch(const DecodeParams &p, hipStream_t stream) {
       (int64_t)p.num_parts * p.num_seqs * (p.num_q_heads / GH);
   if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  // the grouped kernel steps over whole blocks of whole wave-wide loads
-  if constexpr (GH == 8 && !DecodeShape<D, BS>::SUB)
+  // 8 heads per KV head: matrix-core tiles of 16 rows inside one block
+  // (block sizes 16 and 32); block size 8 takes the vector-ALU grouped
+  // kernel, which steps over whole blocks of whole wave-wide loads
+  if constexpr (GH == 8 && (BS == 16 || BS == 32))
+    decode_gqa8_mfma_kernel<D, BS><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(p);
+  else if constexpr (GH == 8 && !DecodeShape<D, BS>::SUB)
     decode_gqa8_kernel<D, BS><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(p);
   else
     decode_kernel<D, BS, GH>

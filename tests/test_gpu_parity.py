@@ -52,6 +52,11 @@ SMALL_DECODE = [
     gpu_spec("d128_bs8_gqa2", 4, 2, 128, 8, EDGE_LENS, seed=9),
     gpu_spec("d128_bs8_gqa8", 16, 2, 128, 8, EDGE_LENS, seed=10),
     gpu_spec("d64_bs8_mha", 4, 4, 64, 8, EDGE_LENS, seed=16),
+    # 8 query heads per KV head on the matrix cores: both head dims, both
+    # block sizes with 16-row tiles
+    gpu_spec("d128_bs16_gqa8", 16, 2, 128, 16, EDGE_LENS, seed=18),
+    gpu_spec("d64_bs16_gqa8", 8, 1, 64, 16, EDGE_LENS, seed=19),
+    gpu_spec("d64_bs32_gqa8", 16, 2, 64, 32, EDGE_LENS, seed=20),
 ]
 
 
