@@ -13,13 +13,13 @@ using namespace pkv;
 
 namespace {
 
-// Default split: the largest partition (1024, 512 or 256 tokens, at most 64
-// blocks) that still gives at least kTargetWorkgroups decode workgroups of 8
-// waves (4 per CU on the chip's 256 CUs), so long sequences run few, long
-// workgroups, a batch that fills the chip is not split (no merge launch),
-// and short batches are cut until they fill it.
+// Default split: the largest partition (2048, 1024, 512 or 256 tokens, at
+// most 64 blocks, so 1024 at block size 16) that still gives at least
+// kTargetWorkgroups decode workgroups (4 per CU on the chip's 256 CUs), so
+// long sequences run few, long workgroups, a batch that fills the chip is not
+// split (no merge launch), and short batches are cut until they fill it.
 constexpr int kTargetWorkgroups = 1024;
-constexpr int kPartitionChoices[] = {1024, 512, 256};
+constexpr int kPartitionChoices[] = {2048, 1024, 512, 256};
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 

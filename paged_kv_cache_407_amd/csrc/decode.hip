@@ -618,10 +618,12 @@ __global__ __launch_bounds__(256) void decode_gqa8_mfma_kernel(DecodeParams p) {
   const int kcol = lane % SLOTS, krow = lane / SLOTS;  // K load layout
   uint4 *Kw = sK[wave];
 
-  for (int b = blk0 + wave * CH; b < blk1; b += NW * CH) {
-    const int tok0 = b * BS;
-    uint4 kr[2][KNI];       // K: tile i, row q*KRPI + krow, chunk kcol
-    uint32_t vr[2][4][VD / 2];  // V: tile i, token tok0 + 16i + 4g + r
+  // One wave step: 32 tokens starting at block b.  (Issuing each step's loads
+  // one step ahead, in a second register buffer, measured no faster: it
+  // costs a wave per SIMD.)
+  using KRegs = uint4[2][KNI];           // K: tile i, row q*KRPI + krow, chunk kcol
+  using VRegs = uint32_t[2][4][VD / 2];  // V: tile i, token 16i + 4g + r of the step
+  auto load_step = [&](int b, KRegs &kr, VRegs &vr) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int bi = (16 * i) / BS;  // block of the tile within the step
@@ -645,6 +647,9 @@ __global__ __launch_bounds__(256) void decode_gqa8_mfma_kernel(DecodeParams p) {
         }
       }
     }
+  };
+  auto compute_step = [&](int b, KRegs &kr, VRegs &vr) {
+    const int tok0 = b * BS;
     const bool full = tok0 + TOK <= tok_end;
     // K through the wave's LDS tile: stored as loaded (16 lanes per row),
     // read back in the operand layout (4 lanes per row).  Chunk c of row t
@@ -729,6 +734,13 @@ __global__ __launch_bounds__(256) void decode_gqa8_mfma_kernel(DecodeParams p) {
       acc[mt] = mfma16x16x32(va, phi, acc[mt]);
       acc[mt] = mfma16x16x32(va, plo, acc[mt]);
     }
+  };
+
+  KRegs kr;
+  VRegs vr;
+  for (int b = blk0 + wave * CH; b < blk1; b += NW * CH) {
+    load_step(b, kr, vr);
+    compute_step(b, kr, vr);
   }
 
   // the 4 lanes of a head hold sums over different tokens

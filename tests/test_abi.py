@@ -56,15 +56,16 @@ def test_partition_and_workspace_policy():
     # short sequences are not split and need no workspace
     assert pkv.decode_partition_size(32, 32, 32, 128, 16, 200) == 208
     assert pkv.decode_workspace_size(32, 32, 32, 128, 16, 200) == 0
-    # the largest of 1024 / 512 / 256 tokens that still gives at least 1024
-    # workgroups; a sequence that fits one partition is not split
+    # the largest of 2048 / 1024 / 512 / 256 tokens (at most 64 blocks) that
+    # still gives at least 1024 workgroups; a sequence that fits one
+    # partition is not split
     assert pkv.decode_partition_size(8, 32, 32, 128, 16, 32768) == 1024      # 8 x 32K
     assert pkv.decode_partition_size(60, 32, 32, 128, 16, 2031) == 1024      # mixed step
     assert pkv.decode_partition_size(32, 32, 32, 128, 16, 1017) == 1024      # batch 32
     assert pkv.decode_workspace_size(32, 32, 32, 128, 16, 1017) == 0
     assert pkv.decode_partition_size(4, 32, 32, 128, 16, 1017) == 256        # batch 4
     assert pkv.decode_partition_size(8, 32, 32, 128, 16, 2048) == 512        # batch 8
-    assert pkv.decode_partition_size(256, 64, 8, 128, 32, 4096) == 1024      # GQA 64/8
+    assert pkv.decode_partition_size(256, 64, 8, 128, 32, 4096) == 2048      # GQA 64/8
     ws = pkv.decode_workspace_size(8, 32, 32, 128, 16, 32768)
     rows = 8 * 32 * 32
     assert ws >= rows * (128 + 2) * 4
