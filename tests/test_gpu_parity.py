@@ -221,16 +221,27 @@ def test_decode_dispatch_order_is_bitwise_neutral(name):
     check_decode(b, kc, vc, to_host(dev.decode(seq_order=orders[0])))
 
 
-def test_decode_permutation_invariance_bitwise():
-    b = W.make_batch("llama_decode")
+# 8 query heads per KV head at block size 32 with a shared prefix: the
+# matrix-core decode, small enough to relabel on the host
+GQA_PERM = W.Spec(name="gqa_perm", num_q_heads=16, num_kv_heads=2, head_dim=128,
+                  block_size=32, num_blocks=640, seed=21, decode_count=24,
+                  decode_dist="uniform", decode_lo=20, decode_hi=700, shared_prefix=64)
+
+
+@pytest.mark.parametrize("spec,part", [("llama_decode", 0), (GQA_PERM, 0), (GQA_PERM, 64)],
+                         ids=["llama_decode", "gqa8_bs32", "gqa8_bs32_split"])
+def test_decode_permutation_invariance_bitwise(spec, part):
+    b = W.make_batch(spec)
     dev = DevBatch(b)
     dev.append()
-    o1 = to_host(dev.decode())
+    o1 = to_host(dev.decode(partition_size=part))
     kc, vc = to_host(dev.k_cache), to_host(dev.v_cache)
     kc2, vc2, t2 = pins.relabel_blocks(np.random.default_rng(5), b, kc, vc)
-    o2 = to_host(dev.decode(tables=to_dev(t2["tables_dec"]), k_cache=to_dev(kc2),
-                            v_cache=to_dev(vc2)))
+    o2 = to_host(dev.decode(partition_size=part, tables=to_dev(t2["tables_dec"]),
+                            k_cache=to_dev(kc2), v_cache=to_dev(vc2)))
     assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
+    if spec is GQA_PERM:
+        check_decode(b, kc, vc, o1)
 
 
 def test_decode_sharing_invariance_bitwise():
@@ -528,9 +539,10 @@ def test_decode_workspace_reuse_across_shapes():
             assert np.array_equal(o.view(np.uint32), first.view(np.uint32))
 
 
-def test_decode_graph_replays_match_eager():
+@pytest.mark.parametrize("name", ["llama_decode", "gqa_shared"])
+def test_decode_graph_replays_match_eager(name):
     say("decode graph replays")
-    b = W.make_batch("llama_decode")
+    b = W.make_batch(name)
     dev = DevBatch(b)
     dev.append()
     import paged_kv_cache_407_amd as pkv
