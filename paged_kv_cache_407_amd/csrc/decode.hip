@@ -738,7 +738,15 @@ __global__ __launch_bounds__(256) void decode_gqa8_mfma_kernel(DecodeParams p) {
 
   KRegs kr;
   VRegs vr;
-  for (int b = blk0 + wave * CH; b < blk1; b += NW * CH) {
+  // The partition's steps are walked from an offset given by the sequence
+  // index, so that workgroups running side by side read different blocks of
+  // a prefix their sequences share (fewer requests piling onto the same L2
+  // lines at once).  The order depends on the sequence alone, so results do
+  // not depend on the dispatch order or on where blocks sit in the pool.
+  const int nsteps = cdiv(blk1 - blk0, CH);
+  const int rot = s % nsteps;
+  for (int j = wave; j < nsteps; j += NW) {
+    const int b = blk0 + CH * (j + rot < nsteps ? j + rot : j + rot - nsteps);
     load_step(b, kr, vr);
     compute_step(b, kr, vr);
   }
@@ -785,26 +793,62 @@ __global__ __launch_bounds__(256) void decode_gqa8_mfma_kernel(DecodeParams p) {
   }
 }
 
+// One thread per (row, 4 dims): 256 / (D/4) rows per workgroup.  A row split
+// into at most kMergeFast partitions issues all its workspace loads at once
+// (one memory round trip after the length); longer rows take the maximum
+// first, then the sums.  Both forms add in partition order, so a row's
+// result does not depend on which form ran.
+constexpr int kMergeFast = 4;
 template <int D, int BS>
-__global__ __launch_bounds__(D) void decode_merge_kernel(DecodeParams p) {
-  const size_t row = blockIdx.x;
+__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
+  constexpr int D4 = D / 4, RPW = 256 / D4;
+  const size_t row = (size_t)blockIdx.x * RPW + threadIdx.x / D4;
+  const size_t rows = (size_t)p.num_seqs * p.num_q_heads;
+  if (row >= rows) return;
   const int s = (int)(row / p.num_q_heads);
-  const int d = threadIdx.x;
+  const int d = 4 * ((int)threadIdx.x % D4);
   const int L = p.seq_lens[s];
   if (!(L >= 1 && L <= p.max_seq_len && L <= p.max_blocks_per_seq * BS))
     return;  // the partition kernel wrote NaN
   const int np = cdiv(L, p.part_tokens);
   if (np == 1) return;  // written directly by the partition kernel
   const size_t base = row * p.num_parts;
-  float M = -INFINITY;
-  for (int j = 0; j < np; ++j) M = fmaxf(M, p.ws_m[base + j]);
-  float o = 0.f, l = 0.f;
-  for (int j = 0; j < np; ++j) {
-    const float e = fast_exp2(p.ws_m[base + j] - M);
-    o = fmaf(e, p.ws_o[(base + j) * D + d], o);
-    l = fmaf(e, p.ws_l[base + j], l);
+  float M = -INFINITY, l = 0.f;
+  f4_t o = f4_t{0.f, 0.f, 0.f, 0.f};
+  if (np <= kMergeFast) {
+    // a partition index past the row's last is clamped to 0 (in bounds,
+    // unused)
+    float mj[kMergeFast], lj[kMergeFast];
+    f4_t oj[kMergeFast];
+#pragma unroll
+    for (int j = 0; j < kMergeFast; ++j) {
+      const size_t pi = base + (j < np ? j : 0);
+      mj[j] = p.ws_m[pi];
+      lj[j] = p.ws_l[pi];
+      oj[j] = *reinterpret_cast<const f4_t *>(p.ws_o + pi * D + d);
+    }
+#pragma unroll
+    for (int j = 0; j < kMergeFast; ++j)
+      if (j < np) M = fmaxf(M, mj[j]);
+#pragma unroll
+    for (int j = 0; j < kMergeFast; ++j)
+      if (j < np) {
+        const float e = fast_exp2(mj[j] - M);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) o[k] = fmaf(e, oj[j][k], o[k]);
+        l = fmaf(e, lj[j], l);
+      }
+  } else {
+    for (int j = 0; j < np; ++j) M = fmaxf(M, p.ws_m[base + j]);
+    for (int j = 0; j < np; ++j) {
+      const float e = fast_exp2(p.ws_m[base + j] - M);
+      const f4_t v = *reinterpret_cast<const f4_t *>(p.ws_o + (base + j) * D + d);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) o[k] = fmaf(e, v[k], o[k]);
+      l = fmaf(e, p.ws_l[base + j], l);
+    }
   }
-  p.out[row * D + d] = o / l;
+  *reinterpret_cast<f4_t *>(p.out + row * D + d) = o / l;
 }
 
 template <int D, int BS, int GH>
@@ -826,7 +870,8 @@ static hipError_t launch(const DecodeParams &p, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.num_parts == 1) return e;
   const int64_t rows = (int64_t)p.num_seqs * p.num_q_heads;
-  decode_merge_kernel<D, BS><<<dim3((unsigned)rows), dim3(D), 0, stream>>>(p);
+  constexpr int RPW = 256 / (D / 4);  // rows per merge workgroup
+  decode_merge_kernel<D, BS><<<dim3((unsigned)((rows + RPW - 1) / RPW)), dim3(256), 0, stream>>>(p);
   return hipGetLastError();
 }
 
