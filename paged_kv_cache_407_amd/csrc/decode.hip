@@ -796,8 +796,9 @@ __global__ __launch_bounds__(256) void decode_gqa8_mfma_kernel(DecodeParams p) {
 // One thread per (row, 4 dims): 256 / (D/4) rows per workgroup.  A row split
 // into at most kMergeFast partitions issues all its workspace loads at once
 // (one memory round trip after the length); longer rows take the maximum
-// first, then the sums.  Both forms add in partition order, so a row's
-// result does not depend on which form ran.
+// first, then the sums, with each chunk's loads issued together.  Both forms
+// add in partition order, so a row's result does not depend on which form
+// ran.
 constexpr int kMergeFast = 4;
 template <int D, int BS>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
@@ -839,13 +840,34 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
         l = fmaf(e, lj[j], l);
       }
   } else {
-    for (int j = 0; j < np; ++j) M = fmaxf(M, p.ws_m[base + j]);
-    for (int j = 0; j < np; ++j) {
-      const float e = fast_exp2(p.ws_m[base + j] - M);
-      const f4_t v = *reinterpret_cast<const f4_t *>(p.ws_o + (base + j) * D + d);
+    // the same two passes, each chunk's loads issued together
+    for (int j0 = 0; j0 < np; j0 += 2 * kMergeFast) {
+      float mj[2 * kMergeFast];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) o[k] = fmaf(e, v[k], o[k]);
-      l = fmaf(e, p.ws_l[base + j], l);
+      for (int u = 0; u < 2 * kMergeFast; ++u)
+        mj[u] = p.ws_m[base + (j0 + u < np ? j0 + u : 0)];
+#pragma unroll
+      for (int u = 0; u < 2 * kMergeFast; ++u)
+        if (j0 + u < np) M = fmaxf(M, mj[u]);
+    }
+    for (int j0 = 0; j0 < np; j0 += kMergeFast) {
+      float mj[kMergeFast], lj[kMergeFast];
+      f4_t oj[kMergeFast];
+#pragma unroll
+      for (int u = 0; u < kMergeFast; ++u) {
+        const size_t pi = base + (j0 + u < np ? j0 + u : 0);
+        mj[u] = p.ws_m[pi];
+        lj[u] = p.ws_l[pi];
+        oj[u] = *reinterpret_cast<const f4_t *>(p.ws_o + pi * D + d);
+      }
+#pragma unroll
+      for (int u = 0; u < kMergeFast; ++u)
+        if (j0 + u < np) {
+          const float e = fast_exp2(mj[u] - M);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) o[k] = fmaf(e, oj[u][k], o[k]);
+          l = fmaf(e, lj[u], l);
+        }
     }
   }
   *reinterpret_cast<f4_t *>(p.out + row * D + d) = o / l;
