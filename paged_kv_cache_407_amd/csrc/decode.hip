@@ -1,4 +1,5 @@
-// Paged attention decode on the vector ALUs.
+// Paged attention decode: on the vector ALUs, and on the matrix cores when 8
+// query heads share each KV head.
 //
 // What is computed ("LLM 推理引擎 Continuous Batching 与 PagedAttention：从
 // vLLM 原理到生产级部署实战", §3.3): for each sequence and query head, the
@@ -267,252 +268,6 @@ __global__ __launch_bounds__((64 * DecodeShape<D, BS>::NW)) void decode_kernel(D
   }
 }
 
-// Decode for 8 query heads per KV head (grouped-query attention).
-//
-// At 8 heads the vector ALUs, not HBM, bound the kernel above, so the score
-// step is laid out differently: each wave step's 32 K rows are staged into a
-// wave-private LDS tile and read back transposed, 4 lanes per token (D/4
-// dims each), so a head's score needs two DPP adds (not four per row), and
-// each (token, head) weight is exponentiated once instead of once per lane
-// of a 16-lane row.  The weights go to the lanes that hold the V rows (the
-// coalesced load layout, unchanged) through a 1 KB LDS buffer read as
-// broadcasts, and PV accumulates exactly as in decode_kernel.  The 8 heads'
-// query rows sit in LDS (128 VGPRs of registers otherwise).  K tile slots
-// are XOR-swizzled so the tile stores and the transposed reads are free of
-// LDS bank conflicts.  The running maximum of a head is wave-uniform and
-// only moves when a score exceeds it by more than 2^8.
-template <int D, int BS>
-__global__ __launch_bounds__(256) void decode_gqa8_kernel(DecodeParams p) {
-  constexpr int GH = 8, NW = 4;
-  constexpr int LPR = D / 8, RPL = kWave / LPR;   // load layout
-  constexpr int TOK = 32;                          // tokens per wave step
-  constexpr int CH = TOK / BS, LPB = BS / RPL, NL = CH * LPB;
-  constexpr int SLOTS = D / 8;                     // 16-byte slots per K row
-  constexpr int KQ = D / 32;                       // slots per lane (4 lanes/token)
-  static_assert(TOK % BS == 0 && BS % RPL == 0, "step of whole blocks");
-  __shared__ uint4 sK[NW][TOK * SLOTS];
-  __shared__ __attribute__((aligned(16))) float sP[NW][TOK * GH];
-  __shared__ uint4 sQ[GH * SLOTS];
-  __shared__ float s_acc[NW][GH][D];
-  __shared__ float s_m[NW][GH], s_l[NW][GH];
-
-  const int lane = threadIdx.x & 63;
-  const int wave = uniform(threadIdx.x >> 6);
-  const int HG = p.num_q_heads / GH;
-  int idx = blockIdx.x;
-  const int hg = idx % HG;
-  idx /= HG;
-  const int slot = idx % p.num_seqs;
-  const int s = p.has_order ? p.order[slot] : slot;
-  const int part = idx / p.num_seqs;
-  const int h0 = hg * GH;
-  const size_t row0 = (size_t)s * p.num_q_heads + h0;
-
-  // Length, block ids (from a clamped table index) and query rows are
-  // loaded together, as in decode_kernel.
-  const int part_blocks = p.part_tokens / BS;
-  const int blk0 = part * part_blocks;
-  const int32_t *trow = p.block_tables + (size_t)s * p.max_blocks_per_seq;
-  const int table_id = trow[min(blk0 + lane, p.max_blocks_per_seq - 1)];
-  const int L = p.seq_lens[s];
-  static_assert(GH * SLOTS <= 256, "one query slot per thread");
-  const int qi = min((int)threadIdx.x, GH * SLOTS - 1);
-  const uint4 qslot = ld16(p.q + (row0 + qi / SLOTS) * D + 8 * (qi % SLOTS));
-
-  if (!(L >= 1 && L <= p.max_seq_len && L <= p.max_blocks_per_seq * BS)) {
-    if (part == 0)
-      for (int i = threadIdx.x; i < GH * D; i += blockDim.x)
-        p.out[row0 * D + i] = __builtin_nanf("");
-    return;
-  }
-  const int np_row = cdiv(L, p.part_tokens);
-  if (part >= np_row) return;
-
-  const int kvh = h0 / p.group;
-  const int nblk = cdiv(L, BS);
-  const int blk1 = min(blk0 + part_blocks, nblk);
-  const int tok_end = min(L, blk1 * BS);
-
-  int my_blk = lane < blk1 - blk0 ? table_id : 0;
-  const bool my_bad =
-      lane < blk1 - blk0 && (my_blk < 0 || my_blk >= p.num_blocks);
-  if (my_bad) my_blk = 0;
-  const bool bad = __any(my_bad);
-
-  if ((int)threadIdx.x < GH * SLOTS) sQ[threadIdx.x] = qslot;
-  __syncthreads();
-
-  // load layout: lane holds 8 dims (slot col) of token rows rrow + RPL*j
-  const int col = lane % LPR, rrow = lane / LPR;
-  // score layout: lane owns slots KQ*qd .. +KQ-1 of token (lane >> 2) + 16 ps
-  const int qd = lane & 3, tq = lane >> 2;
-  auto swz = [](int t) { return KQ == 4 ? (t >> 1) & 3 : (t >> 2) & (KQ - 1); };
-  uint4 *Kw = sK[wave];
-  float *Pw = sP[wave];
-
-  float m[GH], lsum[GH], acc[GH][8];
-#pragma unroll
-  for (int g = 0; g < GH; ++g) {
-    m[g] = -INFINITY;
-    lsum[g] = 0.f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) acc[g][k] = 0.f;
-  }
-  const size_t head_elems = (size_t)BS * D;
-  const uint4 zero = make_uint4(0, 0, 0, 0);
-  const float cs = p.scale_log2e;
-
-  for (int b = blk0 + wave * CH; b < blk1; b += NW * CH) {
-    uint4 kr[NL], vr[NL];
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int bb = b + c;
-      const bool in = bb < blk1;
-      const int phys = __builtin_amdgcn_readlane(my_blk, in ? bb - blk0 : 0);
-      const size_t base =
-          ((size_t)phys * p.num_kv_heads + kvh) * head_elems + rrow * D + col * 8;
-#pragma unroll
-      for (int j = 0; j < LPB; ++j) {
-        if (in) {
-          kr[c * LPB + j] = ld16_nt(p.k_cache + base + (size_t)j * RPL * D);
-          vr[c * LPB + j] = ld16_nt(p.v_cache + base + (size_t)j * RPL * D);
-        } else {
-          kr[c * LPB + j] = zero;
-          vr[c * LPB + j] = zero;
-        }
-      }
-    }
-    const bool full = (b + CH) * BS <= tok_end;
-    const int tok0 = b * BS;
-    // K rows into the wave's tile (token t of the step at row t)
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const int t = (i / LPB) * BS + (i % LPB) * RPL + rrow;
-      Kw[t * SLOTS + (col ^ swz(t))] = kr[i];
-    }
-    // transposed read: two passes of 16 tokens
-    h8_t kq[2][KQ];
-#pragma unroll
-    for (int ps = 0; ps < 2; ++ps) {
-      const int t = 16 * ps + tq;
-#pragma unroll
-      for (int j = 0; j < KQ; ++j)
-        kq[ps][j] = as_h8(Kw[t * SLOTS + ((KQ * qd + j) ^ swz(t))]);
-    }
-    float sc[2][GH];
-#pragma unroll
-    for (int g = 0; g < GH; ++g) {
-      h8_t qh[KQ];
-#pragma unroll
-      for (int j = 0; j < KQ; ++j) qh[j] = as_h8(sQ[g * SLOTS + KQ * qd + j]);
-#pragma unroll
-      for (int ps = 0; ps < 2; ++ps) {
-        float d = 0.f;
-#pragma unroll
-        for (int j = 0; j < KQ; ++j) d = dot8(qh[j], kq[ps][j], d);
-        d += dpp<0xB1>(d);  // quad_perm [1,0,3,2]
-        d += dpp<0x4E>(d);  // quad_perm [2,3,0,1]
-        if (!full && tok0 + 16 * ps + tq >= tok_end) d = -INFINITY;
-        sc[ps][g] = d;
-      }
-    }
-    // running maximum (wave-uniform per head), moved lazily
-#pragma unroll
-    for (int g = 0; g < GH; ++g) {
-      const float cm = fmaxf(sc[0][g], sc[1][g]) * cs;
-      if (__any(cm > m[g] + kLazyRescale)) {
-        float mx = cm;
-#pragma unroll
-        for (int off = 4; off < kWave; off <<= 1) mx = xor_max(mx, off);
-        const float mnew = fmaxf(m[g], mx);
-        const float alpha = mnew > m[g] ? fast_exp2(m[g] - mnew) : 1.f;
-        m[g] = mnew;
-        lsum[g] *= alpha;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) acc[g][k] *= alpha;
-      }
-    }
-    // weights: once per (token, head); lane qd = 0 of each quad publishes
-#pragma unroll
-    for (int ps = 0; ps < 2; ++ps) {
-      const bool ok = full || tok0 + 16 * ps + tq < tok_end;
-      float w[GH];
-#pragma unroll
-      for (int g = 0; g < GH; ++g) {
-        const float e = fast_exp2(fmaf(sc[ps][g], cs, -m[g]));
-        w[g] = ok ? e : 0.f;  // select: m may be -inf before any valid token
-        lsum[g] += w[g];
-      }
-      if (qd == 0) {
-        f4_t *dst = reinterpret_cast<f4_t *>(Pw + (16 * ps + tq) * GH);
-        dst[0] = f4_t{w[0], w[1], w[2], w[3]};
-        dst[1] = f4_t{w[4], w[5], w[6], w[7]};
-      }
-    }
-    // PV in the load layout
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const int t = (i / LPB) * BS + (i % LPB) * RPL + rrow;
-      const f4_t *src = reinterpret_cast<const f4_t *>(Pw + t * GH);
-      const f4_t wa = src[0], wb = src[1];
-      const float w[GH] = {wa[0], wa[1], wa[2], wa[3], wb[0], wb[1], wb[2], wb[3]};
-      // masked rows carry weight 0 but may hold NaN: select, never multiply
-      const h8_t v = as_h8((full || tok0 + t < tok_end) ? vr[i] : zero);
-#pragma unroll
-      for (int g = 0; g < GH; ++g)
-#pragma unroll
-        for (int k = 0; k < 8; ++k) acc[g][k] = fmaf(w[g], (float)v[k], acc[g][k]);
-    }
-  }
-
-  // lsum: the 4 lanes of a quad hold equal sums; add the 16 quads.
-  // acc: lanes of one row group hold partial sums over different tokens.
-#pragma unroll
-  for (int g = 0; g < GH; ++g) {
-#pragma unroll
-    for (int off = 4; off < kWave; off <<= 1) lsum[g] = xor_sum(lsum[g], off);
-#pragma unroll
-    for (int off = LPR; off < kWave; off <<= 1)
-#pragma unroll
-      for (int k = 0; k < 8; ++k) acc[g][k] = xor_sum(acc[g][k], off);
-    if (lane < LPR) {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) s_acc[wave][g][col * 8 + k] = acc[g][k];
-    }
-    if (lane == 0) {
-      s_m[wave][g] = m[g];
-      s_l[wave][g] = lsum[g];
-    }
-  }
-  __syncthreads();
-
-  const bool split = np_row > 1;
-  for (int i = threadIdx.x; i < GH * D; i += blockDim.x) {
-    const int g = i / D, d = i % D;
-    float M = s_m[0][g];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) M = fmaxf(M, s_m[w][g]);
-    float o = 0.f, l = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float e = s_m[w][g] > -INFINITY ? fast_exp2(s_m[w][g] - M) : 0.f;
-      o = fmaf(e, s_acc[w][g][d], o);
-      l = fmaf(e, s_l[w][g], l);
-    }
-    if (bad) o = __builtin_nanf("");
-    if (!split) {
-      p.out[(row0 + g) * D + d] = o / l;
-    } else {
-      const size_t pi = (row0 + g) * p.num_parts + part;
-      p.ws_o[pi * D + d] = o;
-      if (d == 0) {
-        p.ws_m[pi] = M;
-        p.ws_l[pi] = l;
-      }
-    }
-  }
-}
-
 // Decode for 8 query heads per KV head on the matrix cores.
 //
 // With 8 query heads sharing every K/V row, the scores of a 32-token step
@@ -540,8 +295,9 @@ __global__ __launch_bounds__(256) void decode_gqa8_kernel(DecodeParams p) {
 // * The fp32 weights enter the PV as an fp16 high part and an fp16 low part
 //   (two MFMAs), so the product keeps about 22 bits of each weight, as fp32
 //   accumulation on the vector ALUs would.
-// * Softmax runs in base 2 with a lazily moved running maximum, as in
-//   decode_gqa8_kernel; masked tokens are removed by selection.
+// * Softmax runs in base 2 with a running maximum that only moves when a
+//   head's maximum exceeds it by 2^8; masked tokens are removed by
+//   selection.
 template <int D, int BS>
 __global__ __launch_bounds__(256) void decode_gqa8_mfma_kernel(DecodeParams p) {
   constexpr int GH = 8, NW = 4;
@@ -552,7 +308,8 @@ __global__ __launch_bounds__(256) void decode_gqa8_mfma_kernel(DecodeParams p) {
   constexpr int SLOTS = D / 8;         // 16-byte chunks of a row
   constexpr int KRPI = kWave / SLOTS;  // K rows per coalesced wave-wide load
   constexpr int KNI = 16 / KRPI;       // K loads per lane per 16-row tile
-  static_assert(BS == 16 || BS == 32, "16-row tiles inside one block");
+  static_assert(BS == 8 || BS == 16 || BS == 32, "a 16-row tile in one or two blocks");
+  constexpr bool TWO = BS < 16;  // a tile spans two blocks
   static_assert(D == 64 || D == 128, "head_dim 64 or 128");
   __shared__ uint4 sK[NW][TOK * SLOTS];  // wave-private K tile, swizzled
   __shared__ float s_acc[NW][GH][D];
@@ -623,28 +380,55 @@ __global__ __launch_bounds__(256) void decode_gqa8_mfma_kernel(DecodeParams p) {
   // costs a wave per SIMD.)
   using KRegs = uint4[2][KNI];           // K: tile i, row q*KRPI + krow, chunk kcol
   using VRegs = uint32_t[2][4][VD / 2];  // V: tile i, token 16i + 4g + r of the step
+  // VD fp16 of one V row (16 or 8 bytes), or zeros
+  auto load_v = [&](uint32_t (&dst)[VD / 2], bool in, const _Float16 *src) {
+    if constexpr (VD == 8) {
+      const uint4 v = in ? ld16_nt(src) : zero;
+      dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
+    } else {
+      const uint2 v = in ? ld8_nt(src) : make_uint2(0, 0);
+      dst[0] = v.x; dst[1] = v.y;
+    }
+  };
   auto load_step = [&](int b, KRegs &kr, VRegs &vr) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int bi = (16 * i) / BS;  // block of the tile within the step
-      const bool in = b + bi < blk1;
-      const int phys = __builtin_amdgcn_readlane(my_blk, in ? b + bi - blk0 : 0);
-      const size_t base = ((size_t)phys * p.num_kv_heads + kvh) * head_elems +
-                          (size_t)((16 * i) % BS) * D;
-      const _Float16 *kb = p.k_cache + base + (size_t)krow * D + 8 * kcol;
-      const _Float16 *vb = p.v_cache + base + (size_t)(4 * g) * D + VD * hc;
+      if constexpr (!TWO) {
+        // tile i lies in block b + 16i/BS, from its row 16i % BS
+        const int bi = (16 * i) / BS;
+        const bool in = b + bi < blk1;
+        const int phys = __builtin_amdgcn_readlane(my_blk, in ? b + bi - blk0 : 0);
+        const size_t base = ((size_t)phys * p.num_kv_heads + kvh) * head_elems +
+                            (size_t)((16 * i) % BS) * D;
+        const _Float16 *kb = p.k_cache + base + (size_t)krow * D + 8 * kcol;
+        const _Float16 *vb = p.v_cache + base + (size_t)(4 * g) * D + VD * hc;
 #pragma unroll
-      for (int q = 0; q < KNI; ++q)
-        kr[i][q] = in ? ld16_nt(kb + (size_t)q * KRPI * D) : zero;
+        for (int q = 0; q < KNI; ++q)
+          kr[i][q] = in ? ld16_nt(kb + (size_t)q * KRPI * D) : zero;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if constexpr (VD == 8) {
-          const uint4 v = in ? ld16_nt(vb + (size_t)r * D) : zero;
-          vr[i][r][0] = v.x; vr[i][r][1] = v.y; vr[i][r][2] = v.z; vr[i][r][3] = v.w;
-        } else {
-          const uint2 v = in ? ld8_nt(vb + (size_t)r * D) : make_uint2(0, 0);
-          vr[i][r][0] = v.x; vr[i][r][1] = v.y;
+        for (int r = 0; r < 4; ++r) load_v(vr[i][r], in, vb + (size_t)r * D);
+      } else {
+        // block size 8: rows 0-7 of tile i in block A = b + 2i, rows 8-15 in
+        // block B = b + 2i + 1.  K load q holds rows q*KRPI .. +KRPI-1 (one
+        // block); V row 4g + r is in block B for g >= 2.
+        const int bA = b + 2 * i, bB = bA + 1;
+        const bool inA = bA < blk1, inB = bB < blk1;
+        const int phA = __builtin_amdgcn_readlane(my_blk, inA ? bA - blk0 : 0);
+        const int phB = __builtin_amdgcn_readlane(my_blk, inB ? bB - blk0 : 0);
+        const size_t baseA = ((size_t)phA * p.num_kv_heads + kvh) * head_elems;
+        const size_t baseB = ((size_t)phB * p.num_kv_heads + kvh) * head_elems;
+#pragma unroll
+        for (int q = 0; q < KNI; ++q) {
+          const bool hi = q * KRPI >= BS;
+          const size_t off = (hi ? baseB : baseA) +
+                             (size_t)((q * KRPI + krow) % BS) * D + 8 * kcol;
+          kr[i][q] = (hi ? inB : inA) ? ld16_nt(p.k_cache + off) : zero;
         }
+        const bool vhi = g >= 2;
+        const _Float16 *vb = p.v_cache + (vhi ? baseB : baseA) + VD * hc;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          load_v(vr[i][r], vhi ? inB : inA, vb + (size_t)((4 * g + r) % BS) * D);
       }
     }
   };
@@ -879,13 +663,10 @@ static hipError_t launch(const DecodeParams &p, hipStream_t stream) {
       (int64_t)p.num_parts * p.num_seqs * (p.num_q_heads / GH);
   if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  // 8 heads per KV head: matrix-core tiles of 16 rows inside one block
-  // (block sizes 16 and 32); block size 8 takes the vector-ALU grouped
-  // kernel, which steps over whole blocks of whole wave-wide loads
-  if constexpr (GH == 8 && (BS == 16 || BS == 32))
+  // 8 heads per KV head: matrix-core tiles of 16 rows in one or two blocks
+  // (block sizes 8, 16 and 32); block size 1 takes the vector-ALU kernel
+  if constexpr (GH == 8 && BS >= 8)
     decode_gqa8_mfma_kernel<D, BS><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(p);
-  else if constexpr (GH == 8 && !DecodeShape<D, BS>::SUB)
-    decode_gqa8_kernel<D, BS><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(p);
   else
     decode_kernel<D, BS, GH>
         <<<dim3((unsigned)grid), dim3(64 * DecodeShape<D, BS>::NW), 0, stream>>>(p);
