@@ -657,6 +657,77 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
   *reinterpret_cast<f4_t *>(p.out + row * D + d) = o / l;
 }
 
+// Batches whose rows may hold more than kMergeFast partitions: one
+// workgroup per row.  Thread group j (256 / (D/4) groups of one thread per 4
+// dims) combines partitions j, j + groups, ... in registers, a chunk of
+// kMergeFast partitions' loads at a time, with the running-maximum rescale;
+// the groups' (maximum, sum, output) are then combined through LDS.  A row
+// takes two memory round trips after its length instead of one per chunk.
+template <int D, int BS>
+__global__ __launch_bounds__(256) void decode_merge_wide_kernel(DecodeParams p) {
+  constexpr int D4 = D / 4, NG = 256 / D4;
+  __shared__ float s_gm[NG], s_gl[NG];
+  __shared__ f4_t s_go[NG][D4];
+  const size_t row = blockIdx.x;
+  const int s = (int)(row / p.num_q_heads);
+  const int c = (int)threadIdx.x % D4, grp = (int)threadIdx.x / D4;
+  const int L = p.seq_lens[s];
+  if (!(L >= 1 && L <= p.max_seq_len && L <= p.max_blocks_per_seq * BS))
+    return;  // the partition kernel wrote NaN
+  const int np = cdiv(L, p.part_tokens);
+  if (np == 1) return;  // written directly by the partition kernel
+  const size_t base = row * p.num_parts;
+  float M = -INFINITY, l = 0.f;
+  f4_t o = f4_t{0.f, 0.f, 0.f, 0.f};
+  for (int j0 = grp; j0 < np; j0 += NG * kMergeFast) {
+    float mj[kMergeFast], lj[kMergeFast];
+    f4_t oj[kMergeFast];
+#pragma unroll
+    for (int u = 0; u < kMergeFast; ++u) {
+      const int j = j0 + u * NG;
+      const size_t pi = base + (j < np ? j : 0);  // past the last: in bounds, unused
+      mj[u] = p.ws_m[pi];
+      lj[u] = p.ws_l[pi];
+      oj[u] = *reinterpret_cast<const f4_t *>(p.ws_o + pi * D + 4 * c);
+    }
+    float cm = M;
+#pragma unroll
+    for (int u = 0; u < kMergeFast; ++u)
+      if (j0 + u * NG < np) cm = fmaxf(cm, mj[u]);
+    const float a = fast_exp2(M - cm);  // 0 on the first chunk (M = -inf)
+    o *= a;
+    l *= a;
+#pragma unroll
+    for (int u = 0; u < kMergeFast; ++u)
+      if (j0 + u * NG < np) {
+        const float e = fast_exp2(mj[u] - cm);
+        o += e * oj[u];
+        l += e * lj[u];
+      }
+    M = cm;
+  }
+  // a group with no partition keeps M = -inf, l = 0, o = 0
+  if (c == 0) {
+    s_gm[grp] = M;
+    s_gl[grp] = l;
+  }
+  s_go[grp][c] = o;
+  __syncthreads();
+  if (grp != 0) return;
+  float Mt = s_gm[0];
+#pragma unroll
+  for (int k = 1; k < NG; ++k) Mt = fmaxf(Mt, s_gm[k]);
+  f4_t ot = f4_t{0.f, 0.f, 0.f, 0.f};
+  float lt = 0.f;
+#pragma unroll
+  for (int k = 0; k < NG; ++k) {
+    const float e = s_gm[k] > -INFINITY ? fast_exp2(s_gm[k] - Mt) : 0.f;
+    ot += e * s_go[k][c];
+    lt += e * s_gl[k];
+  }
+  *reinterpret_cast<f4_t *>(p.out + row * D + 4 * c) = ot * (1.f / lt);
+}
+
 template <int D, int BS, int GH>
 static hipError_t launch(const DecodeParams &p, hipStream_t stream) {
   const int64_t grid =
@@ -674,7 +745,10 @@ static hipError_t launch(const DecodeParams &p, hipStream_t stream) {
   if (e != hipSuccess || p.num_parts == 1) return e;
   const int64_t rows = (int64_t)p.num_seqs * p.num_q_heads;
   constexpr int RPW = 256 / (D / 4);  // rows per merge workgroup
-  decode_merge_kernel<D, BS><<<dim3((unsigned)((rows + RPW - 1) / RPW)), dim3(256), 0, stream>>>(p);
+  if (p.num_parts <= kMergeFast)
+    decode_merge_kernel<D, BS><<<dim3((unsigned)((rows + RPW - 1) / RPW)), dim3(256), 0, stream>>>(p);
+  else
+    decode_merge_wide_kernel<D, BS><<<dim3((unsigned)rows), dim3(256), 0, stream>>>(p);
   return hipGetLastError();
 }
 
