@@ -57,6 +57,7 @@ SMALL_DECODE = [
     gpu_spec("d128_bs16_gqa8", 16, 2, 128, 16, EDGE_LENS, seed=18),
     gpu_spec("d64_bs16_gqa8", 8, 1, 64, 16, EDGE_LENS, seed=19),
     gpu_spec("d64_bs32_gqa8", 16, 2, 64, 32, EDGE_LENS, seed=20),
+    gpu_spec("d64_bs8_gqa8", 8, 1, 64, 8, EDGE_LENS, seed=22),
 ]
 
 
