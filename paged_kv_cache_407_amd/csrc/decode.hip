@@ -28,9 +28,9 @@
 //   one VGPR holds the partition's block ids: lane j keeps entry j and a
 //   wave reads it with v_readlane, or, for blocks smaller than one
 //   wave-wide load, each lane fetches its token's entry with a lane
-//   permute).  One workgroup of 4 waves takes one (partition, sequence,
-//   head group); waves take interleaved steps of whole blocks and are merged
-//   through LDS.
+//   permute).  One workgroup of 8 waves (fewer when a partition holds fewer
+//   wave steps) takes one (partition, sequence, head group); waves take
+//   interleaved steps of whole blocks and are merged through LDS.
 // * With several partitions, each workgroup stores (max, sum, unnormalised
 //   output) and decode_merge_kernel combines them: M = max_i m_i,
 //   out = sum_i 2^(m_i-M) o_i / sum_i 2^(m_i-M) l_i -- the rescaling of the
