@@ -123,8 +123,12 @@ int32_t pkv_decode_partition_size(int32_t num_seqs, int32_t num_q_heads,
  *                  that size is 0).  Its contents on entry do not matter and
  *                  nothing in it survives a call; calls that share a
  *                  workspace must not run concurrently.
- * Query heads that share a KV head are served by one workgroup, so each
- * K/V row is read once for all of them.
+ * Up to 8 query heads that share a KV head are served by one workgroup, so
+ * each K/V row is read once for all of them.  With 8 (or a multiple of 8)
+ * query heads per KV head and block_size >= 8, the scores and the weighted
+ * sum run as fp16 matrix-core products with fp32 accumulation; the weights
+ * enter them as an fp16 high part plus an fp16 low part, so the result
+ * keeps fp32-level accuracy.
  */
 int pkv_paged_attention_decode(float *out, const void *q, const void *k_cache,
                                const void *v_cache,
