@@ -33,10 +33,12 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-I", str(ROOT / "include"), "-I", str(CSRC)]
 
 
-# Per-source options.  decode.hip: MFMA accumulators in ordinary VGPRs; the
+# Per-source options.  decode.hip: MFMA accumulators in ordinary VGPRs (the
 # grouped-query decode rescales and stores them with vector ALU code every
-# step, which otherwise copies them between AGPRs and VGPRs around each MFMA.
-SOURCE_FLAGS = {"decode.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
+# step, which otherwise copies them between AGPRs and VGPRs around each
+# MFMA); no type-based alias assumptions, because a wave's LDS K tile (16-byte
+# vectors) is reused for its fp32 partial output.
+SOURCE_FLAGS = {"decode.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form", "-fno-strict-aliasing"]}
 
 
 def _compile(src: Path, verbose: bool) -> Path:

@@ -49,7 +49,7 @@ int32_t partition_tokens(int32_t num_seqs, int32_t num_q_heads,
   if (requested < 0) return 0;
   int64_t rows = (int64_t)(num_seqs > 0 ? num_seqs : 1) * (num_q_heads > 0 ? num_q_heads : 1);
   if (num_q_heads > 0 && num_kv_heads > 0 && num_q_heads % num_kv_heads == 0)
-    rows /= heads_per_workgroup(num_q_heads / num_kv_heads);
+    rows /= heads_per_workgroup(num_q_heads / num_kv_heads, block_size);
   int64_t part = 0;
   for (int choice : kPartitionChoices) {
     part = std::min<int64_t>(round_up(choice, block_size), cap);

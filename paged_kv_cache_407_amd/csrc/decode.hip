@@ -268,14 +268,16 @@ __global__ __launch_bounds__((64 * DecodeShape<D, BS>::NW)) void decode_kernel(D
   }
 }
 
-// Decode for 8 query heads per KV head on the matrix cores.
+// Decode for 8 or 16 query heads per KV head (GH per workgroup) on the
+// matrix cores.
 //
 // With 8 query heads sharing every K/V row, the scores of a 32-token step
 // are the product of an [8 x D] query block with D x 32 keys, and the output
 // update is an [8 x 32] weight block times 32 x D values: dense contractions
 // of 8 FLOP per logical K/V byte, past the point where the vector ALUs (no
 // packed fp32) keep up with HBM.  Both run here as v_mfma_f32_16x16x32_f16
-// tiles, the 8 query heads padded to 16 columns with zeros:
+// tiles with the GH query heads as the 16 columns (8 heads padded with
+// zeros; 16 heads fill them, so one workgroup reads each K/V row for all):
 // * S^T (16 tokens x 16 heads) = K_tile (16 x D) . Q^T.  Lane l supplies
 //   K row l%16, dims 32kk + 8(l/16) .. +7 of k-step kk.  K is loaded with
 //   16 lanes per row (whole rows per load instruction, as V) and handed to
@@ -298,9 +300,10 @@ __global__ __launch_bounds__((64 * DecodeShape<D, BS>::NW)) void decode_kernel(D
 // * Softmax runs in base 2 with a running maximum that only moves when a
 //   head's maximum exceeds it by 2^8; masked tokens are removed by
 //   selection.
-template <int D, int BS>
-__global__ __launch_bounds__(256) void decode_gqa8_mfma_kernel(DecodeParams p) {
-  constexpr int GH = 8, NW = 4;
+template <int D, int BS, int GH>
+__global__ __launch_bounds__(256) void decode_gqa_mfma_kernel(DecodeParams p) {
+  static_assert(GH == 8 || GH == 16, "8 or 16 query heads per workgroup");
+  constexpr int NW = 4;
   constexpr int TOK = 32;        // tokens per wave step: two 16-row tiles
   constexpr int CH = TOK / BS;   // blocks per wave step
   constexpr int KQ = D / 32;     // k-steps of the score product
@@ -311,8 +314,11 @@ __global__ __launch_bounds__(256) void decode_gqa8_mfma_kernel(DecodeParams p) {
   static_assert(BS == 8 || BS == 16 || BS == 32, "a 16-row tile in one or two blocks");
   constexpr bool TWO = BS < 16;  // a tile spans two blocks
   static_assert(D == 64 || D == 128, "head_dim 64 or 128");
-  __shared__ uint4 sK[NW][TOK * SLOTS];  // wave-private K tile, swizzled
-  __shared__ float s_acc[NW][GH][D];
+  // Wave-private K tile (swizzled); after its last step a wave stores its
+  // partial output [GH][D] fp32 in the same place (GH*D*4 <= TOK*SLOTS*16
+  // bytes), so the workgroup needs no LDS beyond its K tiles.
+  __shared__ uint4 sK[NW][TOK * SLOTS];
+  static_assert(GH * D * 4 <= TOK * SLOTS * 16, "partial output fits the K tile");
   __shared__ float s_m[NW][GH], s_l[NW][GH];
 
   const int lane = threadIdx.x & 63;
@@ -341,7 +347,7 @@ __global__ __launch_bounds__(256) void decode_gqa8_mfma_kernel(DecodeParams p) {
   h8_t qv[KQ];
 #pragma unroll
   for (int kk = 0; kk < KQ; ++kk) {
-    const uint4 r = ld16(p.q + (row0 + (hc & 7)) * D + (4 * kk + g) * 8);
+    const uint4 r = ld16(p.q + (row0 + (hc & (GH - 1))) * D + (4 * kk + g) * 8);
     qv[kk] = as_h8(hc < GH ? r : zero);
   }
 
@@ -542,7 +548,7 @@ __global__ __launch_bounds__(256) void decode_gqa8_mfma_kernel(DecodeParams p) {
     for (int r = 0; r < 4; ++r)
 #pragma unroll
       for (int mt = 0; mt < VD; ++mt)
-        s_acc[wave][hc][VD * (4 * g + r) + mt] = acc[mt][r];
+        reinterpret_cast<float *>(sK[wave])[hc * D + VD * (4 * g + r) + mt] = acc[mt][r];
     if (g == 0) {
       s_m[wave][hc] = m;
       s_l[wave][hc] = lsum;
@@ -560,7 +566,7 @@ __global__ __launch_bounds__(256) void decode_gqa8_mfma_kernel(DecodeParams p) {
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
       const float e = s_m[w][h] > -INFINITY ? fast_exp2(s_m[w][h] - M) : 0.f;
-      o = fmaf(e, s_acc[w][h][d], o);
+      o = fmaf(e, reinterpret_cast<const float *>(sK[w])[h * D + d], o);
       l = fmaf(e, s_l[w][h], l);
     }
     if (bad) o = __builtin_nanf("");
@@ -734,10 +740,11 @@ static hipError_t launch(const DecodeParams &p, hipStream_t stream) {
       (int64_t)p.num_parts * p.num_seqs * (p.num_q_heads / GH);
   if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  // 8 heads per KV head: matrix-core tiles of 16 rows in one or two blocks
-  // (block sizes 8, 16 and 32); block size 1 takes the vector-ALU kernel
-  if constexpr (GH == 8 && BS >= 8)
-    decode_gqa8_mfma_kernel<D, BS><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(p);
+  // 8 or 16 heads per workgroup: matrix-core tiles of 16 rows in one or two
+  // blocks (block sizes 8, 16 and 32); block size 1 takes the vector-ALU
+  // kernel
+  if constexpr (GH >= 8 && BS >= 8)
+    decode_gqa_mfma_kernel<D, BS, GH><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(p);
   else
     decode_kernel<D, BS, GH>
         <<<dim3((unsigned)grid), dim3(64 * DecodeShape<D, BS>::NW), 0, stream>>>(p);
@@ -754,7 +761,10 @@ static hipError_t launch(const DecodeParams &p, hipStream_t stream) {
 
 template <int D, int BS>
 static hipError_t launch_heads(const DecodeParams &p, hipStream_t stream) {
-  switch (heads_per_workgroup(p.group)) {
+  switch (heads_per_workgroup(p.group, BS)) {
+    case 16:
+      if constexpr (BS >= 8) return launch<D, BS, 16>(p, stream);
+      return hipErrorInvalidValue;
     case 8: return launch<D, BS, 8>(p, stream);
     case 4: return launch<D, BS, 4>(p, stream);
     case 2: return launch<D, BS, 2>(p, stream);

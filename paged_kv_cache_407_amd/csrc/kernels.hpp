@@ -73,8 +73,10 @@ hipError_t launch_copy_blocks(const CopyParams &p, hipStream_t stream);
 // part_tokens must be a multiple of BS and at most kMaxPartBlocks * BS.
 constexpr int kMaxPartBlocks = 64;
 // Query heads one decode workgroup serves: the largest of 8, 4, 2, 1 that
-// divides the group of query heads sharing one KV head.
-inline int heads_per_workgroup(int group) {
+// divides the group of query heads sharing one KV head, or 16 when 16
+// divides it and the matrix-core kernel serves the block size (>= 8).
+inline int heads_per_workgroup(int group, int block_size) {
+  if (group % 16 == 0 && block_size >= 8) return 16;
   return group % 8 == 0 ? 8 : group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1;
 }
 hipError_t launch_decode(const DecodeParams &p, int head_dim, int block_size,

@@ -58,6 +58,9 @@ SMALL_DECODE = [
     gpu_spec("d64_bs16_gqa8", 8, 1, 64, 16, EDGE_LENS, seed=19),
     gpu_spec("d64_bs32_gqa8", 16, 2, 64, 32, EDGE_LENS, seed=20),
     gpu_spec("d64_bs8_gqa8", 8, 1, 64, 8, EDGE_LENS, seed=22),
+    # 16 query heads per KV head: one matrix-core workgroup per KV head
+    gpu_spec("d128_bs32_gqa16", 32, 2, 128, 32, EDGE_LENS, seed=23),
+    gpu_spec("d64_bs8_gqa16", 16, 1, 64, 8, EDGE_LENS, seed=24),
 ]
 
 
