@@ -124,8 +124,9 @@ int32_t pkv_decode_partition_size(int32_t num_seqs, int32_t num_q_heads,
  *                  nothing in it survives a call; calls that share a
  *                  workspace must not run concurrently.
  * Up to 8 query heads that share a KV head are served by one workgroup, so
- * each K/V row is read once for all of them.  With 8 (or a multiple of 8)
- * query heads per KV head and block_size >= 8, the scores and the weighted
+ * each K/V row is read once for all of them (16 when 16 divide the group
+ * and block_size >= 8).  With 4 or more query heads per KV head (a multiple
+ * of 4) and block_size >= 8, the scores and the weighted
  * sum run as fp16 matrix-core products with fp32 accumulation; the weights
  * enter them as an fp16 high part plus an fp16 low part, so the result
  * keeps fp32-level accuracy.

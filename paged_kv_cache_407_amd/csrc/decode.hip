@@ -268,16 +268,18 @@ __global__ __launch_bounds__((64 * DecodeShape<D, BS>::NW)) void decode_kernel(D
   }
 }
 
-// Decode for 8 or 16 query heads per KV head (GH per workgroup) on the
-// matrix cores.
+// Decode for 4, 8 or 16 query heads per workgroup (GH) sharing one KV head,
+// on the matrix cores.
 //
 // With 8 query heads sharing every K/V row, the scores of a 32-token step
 // are the product of an [8 x D] query block with D x 32 keys, and the output
 // update is an [8 x 32] weight block times 32 x D values: dense contractions
 // of 8 FLOP per logical K/V byte, past the point where the vector ALUs (no
 // packed fp32) keep up with HBM.  Both run here as v_mfma_f32_16x16x32_f16
-// tiles with the GH query heads as the 16 columns (8 heads padded with
-// zeros; 16 heads fill them, so one workgroup reads each K/V row for all):
+// tiles with the GH query heads as the 16 columns (4 or 8 heads padded with
+// zeros; 16 heads fill them, so one workgroup reads each K/V row for all).
+// At 4 heads (4 FLOP per byte) the vector-ALU kernel already falls behind
+// HBM, and the same tiles run at the matrix cores' step rate:
 // * S^T (16 tokens x 16 heads) = K_tile (16 x D) . Q^T.  Lane l supplies
 //   K row l%16, dims 32kk + 8(l/16) .. +7 of k-step kk.  K is loaded with
 //   16 lanes per row (whole rows per load instruction, as V) and handed to
@@ -302,7 +304,7 @@ __global__ __launch_bounds__((64 * DecodeShape<D, BS>::NW)) void decode_kernel(D
 //   selection.
 template <int D, int BS, int GH>
 __global__ __launch_bounds__(256) void decode_gqa_mfma_kernel(DecodeParams p) {
-  static_assert(GH == 8 || GH == 16, "8 or 16 query heads per workgroup");
+  static_assert(GH == 4 || GH == 8 || GH == 16, "4, 8 or 16 query heads per workgroup");
   constexpr int NW = 4;
   constexpr int TOK = 32;        // tokens per wave step: two 16-row tiles
   constexpr int CH = TOK / BS;   // blocks per wave step
@@ -740,10 +742,11 @@ static hipError_t launch(const DecodeParams &p, hipStream_t stream) {
       (int64_t)p.num_parts * p.num_seqs * (p.num_q_heads / GH);
   if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  // 8 or 16 heads per workgroup: matrix-core tiles of 16 rows in one or two
-  // blocks (block sizes 8, 16 and 32); block size 1 takes the vector-ALU
-  // kernel
-  if constexpr (GH >= 8 && BS >= 8)
+  // 4, 8 or 16 heads per workgroup: matrix-core tiles of 16 rows in one or
+  // two blocks (block sizes 8, 16 and 32).  Fewer heads per workgroup, and
+  // block size 1, take the vector-ALU kernel (at 2 heads both run at the
+  // same speed; from 4 heads the vector ALUs fall behind HBM).
+  if constexpr (GH >= 4 && BS >= 8)
     decode_gqa_mfma_kernel<D, BS, GH><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(p);
   else
     decode_kernel<D, BS, GH>

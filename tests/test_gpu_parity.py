@@ -61,6 +61,8 @@ SMALL_DECODE = [
     # 16 query heads per KV head: one matrix-core workgroup per KV head
     gpu_spec("d128_bs32_gqa16", 32, 2, 128, 32, EDGE_LENS, seed=23),
     gpu_spec("d64_bs8_gqa16", 16, 1, 64, 8, EDGE_LENS, seed=24),
+    # 4 query heads per KV head also run on the matrix cores
+    gpu_spec("d64_bs8_gqa4", 8, 2, 64, 8, EDGE_LENS, seed=25),
 ]
 
 
