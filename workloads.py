@@ -102,6 +102,21 @@ SPECS = {
         description="high-concurrency GQA decode: 256 sequences, 64 q / 8 kv "
                     "heads x 128, bs 32, lognormal L (median 1024, clip "
                     "[256,4096]), 512-token prefix shared by all"),
+    # Two more grouped-query shapes, beside the five above: 4 and 16 query
+    # heads per KV head (the group sizes of 32/8- and 128/8-head models),
+    # measured like the others but not part of the contract's five.
+    "gqa4": Spec(
+        name="gqa4", num_q_heads=32, num_kv_heads=8, head_dim=128,
+        block_size=16, num_blocks=64 * 192 + 64, seed=SEED_BASE + 6, decode_count=64,
+        decode_dist="uniform", decode_lo=1024, decode_hi=3072, max_blocks_per_seq=192,
+        description="grouped-query decode, 4 query heads per KV head: 64 sequences, "
+                    "32 q / 8 kv heads x 128, bs 16, L~U[1024,3072]"),
+    "gqa16": Spec(
+        name="gqa16", num_q_heads=128, num_kv_heads=8, head_dim=128,
+        block_size=16, num_blocks=64 * 192 + 64, seed=SEED_BASE + 7, decode_count=64,
+        decode_dist="uniform", decode_lo=1024, decode_hi=3072, max_blocks_per_seq=192,
+        description="grouped-query decode, 16 query heads per KV head: 64 sequences, "
+                    "128 q / 8 kv heads x 128, bs 16, L~U[1024,3072]"),
 }
 
 
