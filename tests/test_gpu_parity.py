@@ -154,7 +154,7 @@ def test_append_zero_tokens():
 
 
 # --------------------------------------------------------------------- decode
-@pytest.mark.parametrize("name", ["tiny", "llama_decode", "gqa_shared"])
+@pytest.mark.parametrize("name", ["tiny", "llama_decode", "gqa_shared", "gqa4", "gqa16"])
 def test_decode_config(name):
     say("decode", name)
     b = W.make_batch(name)
