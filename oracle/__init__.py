@@ -82,18 +82,29 @@ class Oracle:
 
     def kv_append(self, key, value, k_cache, v_cache, slot_mapping):
         """Writes new rows into copies of the pools; returns (k_cache, v_cache)."""
-        key, value = _c(key, np.float16), _c(value, np.float16)
         kc = np.array(k_cache, dtype=np.float16, copy=True, order="C")
         vc = np.array(v_cache, dtype=np.float16, copy=True, order="C")
+        self.kv_append_inplace(key, value, kc, vc, slot_mapping)
+        return kc, vc
+
+    def kv_append_inplace(self, key, value, k_cache, v_cache, slot_mapping):
+        """Writes new rows into the given pools (C-contiguous float16 arrays,
+        modified in place)."""
+        key, value = _c(key, np.float16), _c(value, np.float16)
+        for a in (k_cache, v_cache):
+            if not (isinstance(a, np.ndarray) and a.dtype == np.float16
+                    and a.flags.c_contiguous and a.flags.writeable):
+                raise TypeError("pools must be writeable C-contiguous float16 arrays")
         slot = _c(slot_mapping, np.int32)
-        NB, Hkv, bs, D = kc.shape
+        NB, Hkv, bs, D = k_cache.shape
         T = slot.shape[0]
+        if v_cache.shape != k_cache.shape:
+            raise ValueError("k_cache and v_cache shapes differ")
         if key.shape != (T, Hkv, D) or value.shape != (T, Hkv, D):
             raise ValueError("key/value shape")
-        rc = self.lib.oracle_kv_append(_ptr(key), _ptr(value), _ptr(kc), _ptr(vc),
+        rc = self.lib.oracle_kv_append(_ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache),
                                        _ptr(slot), T, Hkv, D, bs, NB)
         self._check(rc, "kv_append")
-        return kc, vc
 
     def decode(self, q, k_cache, v_cache, block_tables, seq_lens, scale, rows=None):
         """out[s, h, :]; with ``rows`` (ids s*Hq+h) only those rows are

@@ -36,9 +36,8 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
 # Per-source options.  decode.hip: MFMA accumulators in ordinary VGPRs (the
 # grouped-query decode rescales and stores them with vector ALU code every
 # step, which otherwise copies them between AGPRs and VGPRs around each
-# MFMA); no type-based alias assumptions, because a wave's LDS K tile (16-byte
-# vectors) is reused for its fp32 partial output.
-SOURCE_FLAGS = {"decode.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form", "-fno-strict-aliasing"]}
+# MFMA).
+SOURCE_FLAGS = {"decode.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: Path, verbose: bool) -> Path:

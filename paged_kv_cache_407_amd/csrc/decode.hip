@@ -1,5 +1,6 @@
-// Paged attention decode: on the vector ALUs, and on the matrix cores when 8
-// query heads share each KV head.
+// Paged attention decode: on the vector ALUs for one or two query heads per
+// KV head (and at block size 1), on the matrix cores when a workgroup serves
+// 4, 8 or 16 query heads of one KV head at block size 8, 16 or 32.
 //
 // What is computed ("LLM 推理引擎 Continuous Batching 与 PagedAttention：从
 // vLLM 原理到生产级部署实战", §3.3): for each sequence and query head, the
@@ -318,9 +319,15 @@ __global__ __launch_bounds__(256) void decode_gqa_mfma_kernel(DecodeParams p) {
   static_assert(D == 64 || D == 128, "head_dim 64 or 128");
   // Wave-private K tile (swizzled); after its last step a wave stores its
   // partial output [GH][D] fp32 in the same place (GH*D*4 <= TOK*SLOTS*16
-  // bytes), so the workgroup needs no LDS beyond its K tiles.
-  __shared__ uint4 sK[NW][TOK * SLOTS];
-  static_assert(GH * D * 4 <= TOK * SLOTS * 16, "partial output fits the K tile");
+  // bytes), so the workgroup needs no LDS beyond its K tiles.  The two views
+  // are members of one union.
+  union WaveTile {
+    uint4 k[TOK * SLOTS];
+    float o[GH * D];
+  };
+  __shared__ WaveTile sK[NW];
+  static_assert(sizeof(float) * GH * D <= sizeof(uint4) * TOK * SLOTS,
+                "partial output fits the K tile");
   __shared__ float s_m[NW][GH], s_l[NW][GH];
 
   const int lane = threadIdx.x & 63;
@@ -338,7 +345,7 @@ __global__ __launch_bounds__(256) void decode_gqa_mfma_kernel(DecodeParams p) {
   const int g = lane >> 4;   // contraction group of the lane
 
   // Length, block ids (clamped table index) and query rows are loaded
-  // together, as in decode_kernel.  Q^T operand: head hc, zero for hc >= 8
+  // together, as in decode_kernel.  Q^T operand: head hc, zero for hc >= GH
   // (the address is clamped into the head group).
   const int part_blocks = p.part_tokens / BS;
   const int blk0 = part * part_blocks;
@@ -381,7 +388,7 @@ __global__ __launch_bounds__(256) void decode_gqa_mfma_kernel(DecodeParams p) {
   const float cs = p.scale_log2e;
 
   const int kcol = lane % SLOTS, krow = lane / SLOTS;  // K load layout
-  uint4 *Kw = sK[wave];
+  uint4 *Kw = sK[wave].k;
 
   // One wave step: 32 tokens starting at block b.  (Issuing each step's loads
   // one step ahead, in a second register buffer, measured no faster: it
@@ -545,12 +552,17 @@ __global__ __launch_bounds__(256) void decode_gqa_mfma_kernel(DecodeParams p) {
 
   // the 4 lanes of a head hold sums over different tokens
   lsum = sum_over_rows(lsum);
+  // The wave's last K-tile reads come before its partial-output stores into
+  // the same LDS: a compiler fence keeps that order in the code, and LDS
+  // serves one wave's accesses in issue order.
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_wave_barrier();
   if (hc < GH) {
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
       for (int mt = 0; mt < VD; ++mt)
-        reinterpret_cast<float *>(sK[wave])[hc * D + VD * (4 * g + r) + mt] = acc[mt][r];
+        sK[wave].o[hc * D + VD * (4 * g + r) + mt] = acc[mt][r];
     if (g == 0) {
       s_m[wave][hc] = m;
       s_l[wave][hc] = lsum;
@@ -568,7 +580,7 @@ __global__ __launch_bounds__(256) void decode_gqa_mfma_kernel(DecodeParams p) {
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
       const float e = s_m[w][h] > -INFINITY ? fast_exp2(s_m[w][h] - M) : 0.f;
-      o = fmaf(e, reinterpret_cast<const float *>(sK[w])[h * D + d], o);
+      o = fmaf(e, sK[w].o[h * D + d], o);
       l = fmaf(e, s_l[w][h], l);
     }
     if (bad) o = __builtin_nanf("");

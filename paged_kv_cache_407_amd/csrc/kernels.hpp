@@ -69,7 +69,7 @@ struct CopyParams {
   int64_t chunks_per_block;    // num_kv_heads * block_size * head_dim / 8
 };
 hipError_t launch_copy_blocks(const CopyParams &p, hipStream_t stream);
-// D in {64,128}, BS in {16,32}; returns hipErrorInvalidValue otherwise.
+// D in {64,128}, BS in {1,8,16,32}; returns hipErrorInvalidValue otherwise.
 // part_tokens must be a multiple of BS and at most kMaxPartBlocks * BS.
 constexpr int kMaxPartBlocks = 64;
 // Query heads one decode workgroup serves: the largest of 8, 4, 2, 1 that

@@ -149,6 +149,58 @@ def pin_dense_prefill(orc, spec, tol=1e-12):
     return err
 
 
+def pin_dense_config(orc, name, n_rows=48, seed=0, tol=1e-12):
+    """Dense equivalence at a benchmark workload's real shape and pool: the
+    oracle, reading through the block tables of the full batch, against
+    torch's float64 attention over the logical-order K/V the generator drew
+    (for every sequence that owns a sampled row; causal over the whole
+    sequence for prefill chunks).  A seeded sample of n_rows (row, head)
+    pairs of the decode part and of the prefill part, first and last rows
+    included.  The batch's own pools take the append in place."""
+    b = W.make_batch(name, keep_dense=True)
+    kc = np.array(b.k_cache, copy=True)
+    vc = np.array(b.v_cache, copy=True)
+    orc.kv_append_inplace(b.new_k, b.new_v, kc, vc, b.slot_mapping)
+    rng = np.random.default_rng(seed)
+    worst = 0.0
+
+    def sample(n):
+        r = rng.choice(n, size=min(n, n_rows - 2), replace=False)
+        return np.unique(np.concatenate([[0, n - 1], r])).astype(np.int64)
+
+    if b.num_dec:
+        S, Hq, D = b.q_dec.shape
+        rows = sample(S * Hq)
+        got = orc.decode(b.q_dec, kc, vc, b.tables_dec, b.lens_dec, b.scale,
+                         rows=rows).reshape(S * Hq, D)
+        for s in np.unique(rows // Hq):
+            k, v = b.dense[s]
+            ref = sdpa(b.q_dec[s:s + 1], k, v, b.scale)[0]
+            for r in rows[rows // Hq == s]:
+                worst = max(worst, float(np.max(np.abs(got[r] - ref[r % Hq]))))
+    if b.num_pf:
+        T, Hq, D = b.q_pf.shape
+        rows = sample(T * Hq)
+        got = orc.prefill(b.q_pf, b.cu_q_lens, kc, vc, b.tables_pf, b.lens_pf, b.scale,
+                          rows=rows).reshape(T * Hq, D)
+        tok = rows // Hq
+        for c in range(b.num_pf):
+            lo, hi = int(b.cu_q_lens[c]), int(b.cu_q_lens[c + 1])
+            mine = rows[(tok >= lo) & (tok < hi)]
+            if mine.size == 0:
+                continue
+            k, v = b.dense[b.num_dec + c]
+            L = k.shape[0]
+            P = L - (hi - lo)
+            qf = np.zeros((L,) + b.q_pf.shape[1:], np.float16)
+            qf[P:] = b.q_pf[lo:hi]
+            ref = sdpa(qf, k, v, b.scale, causal=True)[P:]
+            for r in mine:
+                worst = max(worst, float(np.max(np.abs(got[r] - ref[r // Hq - lo, r % Hq]))))
+    assert worst <= tol, f"{name}: oracle vs dense attention {worst:.3g}"
+    return worst
+
+
 def _single_seq_pool(rng, L, Hkv, D, bs, k=None, v=None):
     nblk = W.cdiv(L, bs)
     NB = nblk + 2

@@ -21,6 +21,15 @@ def test_dense_decode_tiny_config(orc):
     pins.pin_dense_decode(orc, W.SPECS["tiny"])
 
 
+@pytest.mark.parametrize("name", ["llama_decode", "mixed", "gqa_shared", "long"])
+def test_dense_equivalence_at_config_scale(orc, name):
+    # the paged oracle on sampled rows of the benchmark batches (their real
+    # pools, tables and lengths, including the shared prefix and 32K
+    # contexts) against float64 attention over the contiguous K/V
+    err = pins.pin_dense_config(orc, name)
+    print(f"{name}: oracle vs dense float64 attention {err:.3g}")
+
+
 def test_oracle_rejects_bad_input(orc):
     import oracle
     b = W.make_batch("tiny")
