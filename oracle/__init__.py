@@ -13,12 +13,15 @@ copies with deliberately planted mistakes to show that the pins catch them).
 from __future__ import annotations
 
 import ctypes
+import os
 from pathlib import Path
 
 import numpy as np
 
 _HERE = Path(__file__).resolve().parent
 LIB_PATH = _HERE / "liboracle.so"
+# another build of oracle.c (e.g. with sanitizers) for get()
+LIB_ENV = "PKV_ORACLE_LIB"
 SOURCE_PATH = _HERE / "oracle.c"
 
 _ERRORS = {1: "bad argument", 2: "slot or block id out of range",
@@ -173,9 +176,10 @@ _default: Oracle | None = None
 
 
 def get() -> Oracle:
+    """The oracle built from oracle.c, or the build $PKV_ORACLE_LIB names."""
     global _default
     if _default is None:
-        _default = Oracle()
+        _default = Oracle(os.environ.get(LIB_ENV) or LIB_PATH)
     return _default
 
 

@@ -13,6 +13,7 @@ from __future__ import annotations
 
 import ctypes
 import math
+import os
 from pathlib import Path
 
 import numpy as np
@@ -101,9 +102,38 @@ def load_library(path: str | Path = LIB_PATH):
     return lib
 
 
+# Host-side functions (plain host code): the block manager, the scheduler,
+# the precondition checks and the status strings.
+HOST_LIB_ENV = "PKV_HOST_LIB"
+_HOST_PREFIXES = ("pkv_bm_", "pkv_sched_", "pkv_validate_", "pkv_status_string")
+_host = None
+
+
+def host_library():
+    """The library the host-side functions come from: libpkv.so, or the
+    host-only build of the same sources that $PKV_HOST_LIB names (for
+    example a sanitizer build).  The step executor (pkv_server_*) takes its
+    scheduler and block manager from libpkv.so, so it is not used with such
+    a build."""
+    global _host
+    if _host is None:
+        path = os.environ.get(HOST_LIB_ENV)
+        if not path:
+            _host = load_library()
+        else:
+            lib = ctypes.CDLL(path)
+            for name, (res, args) in SIGNATURES.items():
+                if name.startswith(_HOST_PREFIXES):
+                    fn = getattr(lib, name)
+                    fn.restype = res
+                    fn.argtypes = args
+            _host = lib
+    return _host
+
+
 def _check(rc: int, what: str):
     if rc != PKV_OK:
-        msg = load_library().pkv_status_string(rc).decode()
+        msg = host_library().pkv_status_string(rc).decode()
         raise PkvError(f"{what}: {msg} (status {rc})")
 
 
@@ -306,7 +336,7 @@ def validate_slots(slot_mapping, num_blocks: int, block_size: int) -> None:
     pool and no slot written twice.  Raises PkvError naming the row."""
     sl = _host_i32(slot_mapping, "slot_mapping").reshape(-1)
     bad = ctypes.c_int64(-1)
-    rc = load_library().pkv_validate_slots(sl.ctypes.data, sl.shape[0], int(num_blocks),
+    rc = host_library().pkv_validate_slots(sl.ctypes.data, sl.shape[0], int(num_blocks),
                                            int(block_size), ctypes.byref(bad))
     _validated(rc, bad, "validate_slots")
 
@@ -320,7 +350,7 @@ def validate_tables(block_tables, seq_lens, num_blocks: int, block_size: int) ->
     if t.ndim != 2 or t.shape[0] != L.shape[0]:
         raise ValueError("block_tables must be [S, MB] with S = len(seq_lens)")
     bad = ctypes.c_int64(-1)
-    rc = load_library().pkv_validate_tables(t.ctypes.data, L.ctypes.data, L.shape[0],
+    rc = host_library().pkv_validate_tables(t.ctypes.data, L.ctypes.data, L.shape[0],
                                             t.shape[1], int(num_blocks), int(block_size),
                                             ctypes.byref(bad))
     _validated(rc, bad, "validate_tables")
@@ -335,7 +365,7 @@ def validate_chunks(cu_q_lens, seq_lens, total_q_tokens: int) -> None:
     if cu.shape[0] != L.shape[0] + 1:
         raise ValueError("cu_q_lens must have len(seq_lens) + 1 entries")
     bad = ctypes.c_int64(-1)
-    rc = load_library().pkv_validate_chunks(cu.ctypes.data, L.ctypes.data, L.shape[0],
+    rc = host_library().pkv_validate_chunks(cu.ctypes.data, L.ctypes.data, L.shape[0],
                                             int(total_q_tokens), ctypes.byref(bad))
     _validated(rc, bad, "validate_chunks")
 
@@ -388,7 +418,7 @@ class BlockManager:
     def __init__(self, num_blocks: int, block_size: int):
         import numpy as np
         self._np = np
-        self._lib = load_library()
+        self._lib = host_library()
         self._h = self._lib.pkv_bm_create(int(num_blocks), int(block_size))
         if not self._h:
             raise PkvError("pkv_bm_create: invalid arguments")
@@ -507,7 +537,7 @@ class Scheduler:
                  max_seq_len: int):
         import numpy as np
         self._np = np
-        self._lib = load_library()
+        self._lib = host_library()
         self.bm = block_manager
         self._h = self._lib.pkv_sched_create(block_manager._h, int(max_batch_size),
                                              int(max_num_tokens), int(max_seq_len))

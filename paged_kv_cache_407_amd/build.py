@@ -71,5 +71,26 @@ def build(verbose: bool = False, jobs: int | None = None) -> Path:
     return LIB
 
 
+# Host-only build of the plain host sources with AddressSanitizer and
+# UndefinedBehaviorSanitizer (g++, no device code): the block manager, the
+# scheduler, the precondition checks and the status strings.  The binding
+# takes them from it when $PKV_HOST_LIB names it; load it with libasan
+# preloaded.
+HOST_SOURCES = ("block_manager.cpp", "scheduler.cpp", "validate.cpp")
+HOST_SAN_LIB = HERE / "libpkv_host_asan.so"
+SANITIZE = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+            "-fno-omit-frame-pointer", "-g"]
+
+
+def build_host_sanitized(verbose: bool = False) -> Path:
+    cmd = ["g++", "-O1", "-std=c++17", "-fPIC", "-shared", "-Wall", "-Wextra", *SANITIZE,
+           "-I", str(ROOT / "include"), "-o", str(HOST_SAN_LIB),
+           *(str(CSRC / f) for f in HOST_SOURCES)]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    return HOST_SAN_LIB
+
+
 if __name__ == "__main__":
     build(verbose=True)

@@ -159,17 +159,6 @@ bool copy_shape_ok(int32_t count, int32_t num_kv_heads, int32_t head_dim,
 
 extern "C" {
 
-const char *pkv_status_string(int status) {
-  switch (status) {
-    case PKV_OK: return "ok";
-    case PKV_ERR_INVALID: return "invalid argument";
-    case PKV_ERR_UNSUPPORTED: return "unsupported shape (head_dim 64/128; block_size 1/8/16/32 for decode, 8/16/32 for prefill)";
-    case PKV_ERR_HIP: return "HIP runtime error";
-    case PKV_ERR_NO_BLOCKS: return "not enough free KV blocks";
-    default: return "unknown status";
-  }
-}
-
 int pkv_kv_append(const void *key, const void *value, void *k_cache,
                   void *v_cache, const int32_t *slot_mapping,
                   int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,

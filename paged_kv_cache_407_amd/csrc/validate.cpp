@@ -15,7 +15,8 @@
 // * §4.3 (chunked prefill): a chunk of C new tokens ends its sequence, so
 //   0 <= C <= seq_len, and the chunks' rows are packed in order.
 //
-// Plain host code; no device calls.
+// Plain host code; no device calls.  The status strings of the whole
+// library live here too (host code, also in the host-only builds).
 #include <stdint.h>
 
 #include <algorithm>
@@ -97,6 +98,17 @@ int pkv_validate_chunks(const int32_t *cu_q_lens, const int32_t *seq_lens, int32
   }
   if (cu_q_lens[num_chunks] != total_q_tokens) return fail(bad_index, num_chunks);
   return pass(bad_index);
+}
+
+const char *pkv_status_string(int status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_INVALID: return "invalid argument";
+    case PKV_ERR_UNSUPPORTED: return "unsupported shape (head_dim 64/128; block_size 1/8/16/32 for decode, 8/16/32 for prefill)";
+    case PKV_ERR_HIP: return "HIP runtime error";
+    case PKV_ERR_NO_BLOCKS: return "not enough free KV blocks";
+    default: return "unknown status";
+  }
 }
 
 }  // extern "C"
