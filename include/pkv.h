@@ -48,7 +48,8 @@ enum {
     PKV_ERR_INVALID = 1,     /* null pointer, bad size, misaligned buffer */
     PKV_ERR_UNSUPPORTED = 2, /* no compiled instance for this shape */
     PKV_ERR_HIP = 3,         /* the HIP runtime reported an error */
-    PKV_ERR_NO_BLOCKS = 4    /* block manager: not enough free blocks */
+    PKV_ERR_NO_BLOCKS = 4,   /* block manager: not enough free blocks */
+    PKV_ERR_SCRATCH = 5      /* no-allocation decode: partials exceed its scratch */
 };
 
 /* Static description of a status code. */
@@ -142,6 +143,33 @@ int pkv_paged_attention_decode(float *out, const void *q, const void *k_cache,
                                int32_t partition_size, const int32_t *seq_order,
                                void *workspace, size_t workspace_bytes,
                                void *stream);
+
+/*
+ * The decode above for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments without the workspace, the same kernels
+ * and results.  Split partials go to a device array of the library,
+ * PKV_NOALLOC_SCRATCH_BYTES per GPU, held from the first call on that GPU
+ * until the process ends; the call itself allocates nothing.
+ *   Returns PKV_ERR_SCRATCH, before enqueueing anything, when the partials
+ *   of the call (pkv_decode_workspace_size of its arguments) exceed that
+ *   size; otherwise as pkv_paged_attention_decode.
+ *   Every call on one GPU shares that GPU's array: calls that may overlap
+ *   on one GPU (different streams, or different host threads) race and
+ *   must be ordered by the caller.  Nothing in the array needs to start at
+ *   zero: each call writes the partials it reads.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES (32u << 20)
+int pkv_paged_attention_decode_noalloc(float *out, const void *q, const void *k_cache,
+                                       const void *v_cache,
+                                       const int32_t *block_tables,
+                                       const int32_t *seq_lens, int32_t num_seqs,
+                                       int32_t num_q_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t block_size,
+                                       int32_t num_blocks, int32_t max_blocks_per_seq,
+                                       int32_t max_seq_len, float scale,
+                                       int32_t partition_size, const int32_t *seq_order,
+                                       void *stream);
 
 /*
  * Paged attention prefill of causal chunks whose prefix already sits in

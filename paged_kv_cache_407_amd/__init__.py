@@ -37,6 +37,9 @@ SIGNATURES = {
     "pkv_paged_attention_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32,
                                                   _I32, _I32, _I32, _I32, _F, _I32, _P, _P, _SZ,
                                                   _P]),
+    "pkv_paged_attention_decode_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I32,
+                                                          _I32, _I32, _I32, _I32, _I32, _I32,
+                                                          _F, _I32, _P, _P]),
     "pkv_paged_attention_prefill": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32,
                                                    _I32, _I32, _I32, _I32, _I32, _I32, _I32, _F,
                                                    _P, _SZ, _P]),
@@ -77,6 +80,8 @@ SIGNATURES = {
                                            _I32, _I32, _P]),
 }
 PKV_ERR_NO_BLOCKS = 4
+PKV_ERR_SCRATCH = 5
+NOALLOC_SCRATCH_BYTES = 32 << 20   # PKV_NOALLOC_SCRATCH_BYTES
 
 
 class PkvError(RuntimeError):
@@ -238,6 +243,41 @@ def paged_attention_decode(q, k_cache, v_cache, block_tables, seq_lens, *, max_s
         int(max_seq_len), float(scale), int(partition_size), order_ptr, ws_ptr, ws_bytes,
         _stream(stream))
     _check(rc, "paged_attention_decode")
+    return out
+
+
+def paged_attention_decode_noalloc(q, k_cache, v_cache, block_tables, seq_lens, out, *,
+                                   max_seq_len: int, scale: float | None = None,
+                                   partition_size: int = 0, seq_order=None, stream=None):
+    """The decode of ``paged_attention_decode`` for callers that cannot
+    allocate: ``out`` [S, Hq, D] float32 is required, and the split partials
+    go to the library's per-GPU device scratch (``NOALLOC_SCRATCH_BYTES``)
+    instead of a workspace.  Calls that may overlap on one GPU race on that
+    scratch.  Raises PkvError when the partials exceed it."""
+    NB, Hkv, bs, D = _cache_shape(k_cache, v_cache)
+    _dev(q, "q", torch.float16, 3)
+    _dev(block_tables, "block_tables", torch.int32, 2)
+    _dev(seq_lens, "seq_lens", torch.int32, 1)
+    _dev(out, "out", torch.float32, 3)
+    S, Hq, Dq = q.shape
+    if Dq != D or block_tables.shape[0] != S or seq_lens.shape[0] != S:
+        raise ValueError("q / block_tables / seq_lens shapes disagree")
+    if out.shape != (S, Hq, D):
+        raise ValueError("out shape")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    order_ptr = None
+    if seq_order is not None:
+        seq_order = _host_i32(seq_order, "seq_order").reshape(-1)
+        if seq_order.shape[0] != S:
+            raise ValueError("seq_order must have one entry per sequence")
+        order_ptr = seq_order.ctypes.data
+    rc = load_library().pkv_paged_attention_decode_noalloc(
+        out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        block_tables.data_ptr(), seq_lens.data_ptr(), S, Hq, Hkv, D, bs, NB,
+        block_tables.shape[1], int(max_seq_len), float(scale), int(partition_size), order_ptr,
+        _stream(stream))
+    _check(rc, "paged_attention_decode_noalloc")
     return out
 
 

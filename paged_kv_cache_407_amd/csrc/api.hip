@@ -3,6 +3,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 #include <stdint.h>
 
 #include "common.hpp"
@@ -149,6 +150,39 @@ bool kernel_address(const void *p, const void **out) {
   return false;
 }
 
+// Device scratch of pkv_paged_attention_decode_noalloc: the split
+// partials of one call live in this file-scope array.  Each GPU the library
+// runs on holds its own copy from the first such call until the process
+// ends.  In host code `scratch` names a host-side stand-in, never the device
+// memory: the device address comes from hipGetSymbolAddress, taken once per
+// device with that device current, and only that address is passed on.
+static __device__ __align__(256) char scratch[PKV_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address (taken on its first use).
+int device_scratch(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return PKV_ERR_HIP;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return PKV_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return PKV_OK;
+}
+
 bool copy_shape_ok(int32_t count, int32_t num_kv_heads, int32_t head_dim,
                    int32_t block_size, int32_t src_num_blocks, int32_t dst_num_blocks) {
   return count >= 0 && num_kv_heads > 0 && head_dim > 0 && head_dim % 8 == 0 &&
@@ -274,6 +308,33 @@ int pkv_paged_attention_decode(float *out, const void *q, const void *k_cache,
     p.has_order = 1;
   }
   return hip_status(launch_decode(p, head_dim, block_size, (hipStream_t)stream));
+}
+
+int pkv_paged_attention_decode_noalloc(float *out, const void *q, const void *k_cache,
+                                       const void *v_cache,
+                                       const int32_t *block_tables,
+                                       const int32_t *seq_lens, int32_t num_seqs,
+                                       int32_t num_q_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t block_size,
+                                       int32_t num_blocks, int32_t max_blocks_per_seq,
+                                       int32_t max_seq_len, float scale,
+                                       int32_t partition_size, const int32_t *seq_order,
+                                       void *stream) {
+  // The same argument checks and kernels as pkv_paged_attention_decode; the
+  // partials go to the device's scratch array instead of a caller workspace.
+  const size_t need = pkv_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads,
+                                                head_dim, block_size, max_seq_len,
+                                                partition_size);
+  if (need > (size_t)PKV_NOALLOC_SCRATCH_BYTES) return PKV_ERR_SCRATCH;
+  void *ws = nullptr;
+  if (need > 0) {
+    const int rc = device_scratch(&ws);
+    if (rc != PKV_OK) return rc;
+  }
+  return pkv_paged_attention_decode(out, q, k_cache, v_cache, block_tables, seq_lens,
+                                    num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                    block_size, num_blocks, max_blocks_per_seq, max_seq_len,
+                                    scale, partition_size, seq_order, ws, need, stream);
 }
 
 size_t pkv_prefill_workspace_size(int32_t num_chunks, int32_t total_q_tokens,

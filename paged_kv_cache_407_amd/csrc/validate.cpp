@@ -107,6 +107,9 @@ const char *pkv_status_string(int status) {
     case PKV_ERR_UNSUPPORTED: return "unsupported shape (head_dim 64/128; block_size 1/8/16/32 for decode, 8/16/32 for prefill)";
     case PKV_ERR_HIP: return "HIP runtime error";
     case PKV_ERR_NO_BLOCKS: return "not enough free KV blocks";
+    case PKV_ERR_SCRATCH:
+      return "the call's split partials exceed the no-allocation decode's device scratch "
+             "(PKV_NOALLOC_SCRATCH_BYTES); pass a workspace to pkv_paged_attention_decode";
     default: return "unknown status";
   }
 }
