@@ -48,13 +48,15 @@ constexpr float kLazyRescale = 8.f;
 // of a wave's rows.)
 constexpr float kMaxFloor = -1e30f;
 
-// LDS layout, chosen for this chip's LDS (128 banks of 4 bytes; a 16-byte
-// access is served 32 lanes at a time): the K tile's 16-byte slot of row r is
-// XORed with 2*bit5(r), and lane group g of a QK^T operand supplies the head
-// dimensions of slot KS*g + kk at step kk (any slot-to-k assignment is valid
-// as long as the K and Q operands agree).  With a 17-slot row stride the
-// operand reads and the tile stores are then free of bank conflicts; V^T rows
-// take a 10-slot stride, which makes the PV operand reads conflict-free.
+// LDS layout.  The K tile's 16-byte slot of row r is XORed with 2*bit5(r),
+// and lane group g of a QK^T operand supplies the head dimensions of slot
+// KS*g + kk at step kk (any slot-to-k assignment is valid as long as the K
+// and Q operands agree); with a 17-slot row stride the operand reads are
+// free of bank conflicts, and the tile stores, one whole row per D/8 lanes,
+// are too.  V^T rows take a 10-slot stride, which makes the PV operand reads
+// conflict-free; its stores write one contiguous run of keys per dim row.
+// (Access patterns timed on this chip against contiguous accesses of the
+// same width.)
 __device__ __forceinline__ int ksw(int r) { return (r >> 4) & 2; }
 
 template <int D, int BS>
@@ -114,56 +116,70 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p,
   const int t_lo = sp * ntiles / nparts, t_hi = (sp + 1) * ntiles / nparts;
   const int32_t *trow = p.block_tables + (size_t)c * p.max_blocks_per_seq;
 
-  // Tile loader: thread owns keys KPT*lkg .. +KPT-1 and dims 8*lcc .. +7.
+  // Tile loader: the thread owns KPT consecutive keys of the K tile and
+  // KPT consecutive keys of the V tile, 8 dims (one 16-byte chunk) of each.
+  // K: chunk kcc = tid % (D/8) of keys KPT*kkg .. (kkg = tid / (D/8)), so
+  //    the D/8 lanes of a key row hold the whole row: every load instruction
+  //    reads whole rows and every LDS store writes whole rows (all banks,
+  //    no conflicts).
+  // V: chunk vcc = tid / NKG of keys KPT*vkg .. (vkg = tid % NKG), so the
+  //    lanes with one chunk hold consecutive keys, which the transposed V^T
+  //    store writes as one contiguous run per dim row (no conflicts).
   // It has no branches (a load under a branch makes the compiler wait for
   // it inside the branch, serialising the tile's loads):
-  // * the block id of a later tile is read one tile ahead from a clamped
-  //   (always valid) table index and only checked where it is used; a check
-  //   right after its load would wait for every load issued before it
+  // * the block ids of a later tile are read one tile ahead from clamped
+  //   (always valid) table indices and only checked where they are used; a
+  //   check right after its load would wait for every load issued before it
   //   (memory counters retire in order);
   // * K/V loads are unconditional (an absent key reads block 0, in bounds),
   //   absent keys are zeroed when the tile is stored;
   // * a block id outside the pool sets a per-thread flag, gathered once at
   //   the end.
-  const int lkg = tid % NKG, lcc = tid / NKG;
-  auto lookup = [&](int t) -> int {
-    const int pos = t * BN + KPT * lkg;
+  constexpr int LPR = D / 8;  // 16-byte chunks of a row
+  const int kcc = tid % LPR, kkg = tid / LPR;
+  const int vkg = tid % NKG, vcc = tid / NKG;
+  auto lookup = [&](int t, int kg) -> int {
+    const int pos = t * BN + KPT * kg;
     return trow[min(pos, L - 1) / BS];  // L >= 1, L <= max_blocks_per_seq * BS
   };
   uint4 kreg[KPT], vreg[KPT];
-  unsigned live = 0;  // bit i: key i of this thread's slice exists
-  bool bad = false;   // a block id outside the pool was met
-  auto load = [&](int t, int ph) {
-    // The thread's KPT keys are consecutive and share one block (BS is a
-    // multiple of KPT); the block id is only meaningful when the first of
-    // them lies below L.
-    const int pos = t * BN + KPT * lkg;
+  unsigned klive = 0, vlive = 0;  // bit i: key i of this thread's slice exists
+  bool bad = false;               // a block id outside the pool was met
+  // The thread's KPT keys are consecutive and share one block (BS is a
+  // multiple of KPT); the block id is only meaningful when the first of them
+  // lies below L.  Returns the element offset of the first key's chunk.
+  auto locate = [&](int t, int kg, int cc, int ph, unsigned &live) -> size_t {
+    const int pos = t * BN + KPT * kg;
     const bool want = t < t_hi && pos < L;
     const bool oob = want && (ph < 0 || ph >= p.num_blocks);
     bad |= oob;
     const bool blk = want && !oob;
     live = blk ? (1u << min(L - pos, KPT)) - 1u : 0u;
-    const size_t off =
-        blk ? (((size_t)ph * p.num_kv_heads + kvh) * BS + pos % BS) * D + 8 * lcc
-            : (size_t)8 * lcc;
+    return blk ? (((size_t)ph * p.num_kv_heads + kvh) * BS + pos % BS) * D + 8 * cc
+               : (size_t)8 * cc;
+  };
+  auto load = [&](int t, int phk, int phv) {
+    const size_t koff = locate(t, kkg, kcc, phk, klive);
+    const size_t voff = locate(t, vkg, vcc, phv, vlive);
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-      kreg[i] = ld16(p.k_cache + off + i * D);
-      vreg[i] = ld16(p.v_cache + off + i * D);
+      kreg[i] = ld16(p.k_cache + koff + i * D);
+      vreg[i] = ld16(p.v_cache + voff + i * D);
     }
   };
   auto store = [&](int buf) {
     const uint4 zero = make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-      if (!((live >> i) & 1)) kreg[i] = vreg[i] = zero;
-      const int row = KPT * lkg + i;
-      st16(&sK[buf][row * KSTR + 8 * (lcc ^ ksw(row))], kreg[i]);
+      if (!((klive >> i) & 1)) kreg[i] = zero;
+      if (!((vlive >> i) & 1)) vreg[i] = zero;
+      const int row = KPT * kkg + i;
+      st16(&sK[buf][row * KSTR + 8 * (kcc ^ ksw(row))], kreg[i]);
     }
-    // V^T: dim 8*lcc + j, keys KPT*lkg .. +KPT-1 (KPT*2 contiguous bytes)
+    // V^T: dim 8*vcc + j, keys KPT*vkg .. +KPT-1 (KPT*2 contiguous bytes)
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      _Float16 *dst = &sV[buf][(8 * lcc + j) * VSTR + KPT * lkg];
+      _Float16 *dst = &sV[buf][(8 * vcc + j) * VSTR + KPT * vkg];
       if constexpr (KPT == 4) {
         h4_t t;
 #pragma unroll
@@ -196,8 +212,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p,
   // Prologue, ordered so that only two memory latencies are exposed: the
   // block ids of tiles 0 and 1, then the query rows (issued while the ids
   // are in flight), then tile 0's K/V, which needs its id.
-  int ph_next = lookup(t_lo);
-  const int ph_one = lookup(t_lo + 1);
+  int phk_next = lookup(t_lo, kkg), phv_next = lookup(t_lo, vkg);
+  const int phk_one = lookup(t_lo + 1, kkg), phv_one = lookup(t_lo + 1, vkg);
   // The wave's query rows as B operands: column lc of block qb, dims of
   // slot KS*g + kk (8 per slot).  Rows past the chunk load its last row
   // (unconditional loads, nothing waits inside a branch); their results are
@@ -210,8 +226,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p,
     for (int kk = 0; kk < KS; ++kk)
       qf[kk][qb] = as_h8(ld16(p.q + ((size_t)(q_begin + qr) * Hq + h) * D + 8 * (KS * g + kk)));
   }
-  load(t_lo, ph_next);
-  ph_next = ph_one;
+  load(t_lo, phk_next, phv_next);
+  phk_next = phk_one;
+  phv_next = phv_one;
   store(0);
   __syncthreads();
 
@@ -221,8 +238,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p,
     const int buf = (kt - t_lo) & 1;
     const int kbase = kt * BN;
     // the next tile's loads (harmless past the last tile)
-    load(kt + 1, ph_next);
-    ph_next = lookup(kt + 2);
+    load(kt + 1, phk_next, phv_next);
+    phk_next = lookup(kt + 2, kkg);
+    phv_next = lookup(kt + 2, vkg);
     // skip a tile that lies wholly above this wave's diagonal
     if (wave_live && kbase <= P + wq0 + WROWS - 1) {
       const _Float16 *Kt = sK[buf];
