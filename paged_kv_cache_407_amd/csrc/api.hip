@@ -14,13 +14,14 @@ using namespace pkv;
 
 namespace {
 
-// Default split: the largest partition (2048, 1024, 512 or 256 tokens, at
-// most 64 blocks, so 1024 at block size 16) that still gives at least
-// kTargetWorkgroups decode workgroups (4 per CU on the chip's 256 CUs), so
-// long sequences run few, long workgroups, a batch that fills the chip is not
-// split (no merge launch), and short batches are cut until they fill it.
+// Default split: the largest partition (4096, 2048, 1024, 512 or 256
+// tokens, at most 64 blocks -- 128 on the matrix-core decode -- so 1024 at
+// block size 16 for MHA) that still gives at least kTargetWorkgroups decode
+// workgroups (4 per CU on the chip's 256 CUs), so long sequences run few,
+// long workgroups, a batch that fills the chip is not split (no merge
+// launch), and short batches are cut until they fill it.
 constexpr int kTargetWorkgroups = 1024;
-constexpr int kPartitionChoices[] = {2048, 1024, 512, 256};
+constexpr int kPartitionChoices[] = {4096, 2048, 1024, 512, 256};
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -39,12 +40,16 @@ bool supported_prefill(int32_t head_dim, int32_t block_size) {
 int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 
 // Tokens per partition; 0 when the arguments are invalid.  A partition
-// holds at most kMaxPartBlocks blocks (one VGPR of block ids per wave).
+// holds at most max_partition_blocks() blocks (one or two VGPRs of block
+// ids per wave).
 int32_t partition_tokens(int32_t num_seqs, int32_t num_q_heads,
                          int32_t num_kv_heads, int32_t block_size,
                          int32_t max_seq_len, int32_t requested) {
   if (block_size <= 0 || max_seq_len <= 0) return 0;
-  const int64_t cap = (int64_t)kMaxPartBlocks * block_size;
+  const int group = (num_q_heads > 0 && num_kv_heads > 0 && num_q_heads % num_kv_heads == 0)
+                        ? num_q_heads / num_kv_heads
+                        : 1;
+  const int64_t cap = (int64_t)max_partition_blocks(group, block_size) * block_size;
   if (requested > 0)
     return (requested % block_size || requested > cap) ? 0 : requested;
   if (requested < 0) return 0;

@@ -347,10 +347,12 @@ __global__ __launch_bounds__(256) void decode_gqa_mfma_kernel(DecodeParams p) {
   // Length, block ids (clamped table index) and query rows are loaded
   // together, as in decode_kernel.  Q^T operand: head hc, zero for hc >= GH
   // (the address is clamped into the head group).
+  // A partition holds up to 128 blocks: lane j keeps entries j and 64 + j.
   const int part_blocks = p.part_tokens / BS;
   const int blk0 = part * part_blocks;
   const int32_t *trow = p.block_tables + (size_t)s * p.max_blocks_per_seq;
   const int table_id = trow[min(blk0 + lane, p.max_blocks_per_seq - 1)];
+  const int table_id2 = trow[min(blk0 + kWave + lane, p.max_blocks_per_seq - 1)];
   const int L = p.seq_lens[s];
   const uint4 zero = make_uint4(0, 0, 0, 0);
   h8_t qv[KQ];
@@ -374,11 +376,19 @@ __global__ __launch_bounds__(256) void decode_gqa_mfma_kernel(DecodeParams p) {
   const int blk1 = min(blk0 + part_blocks, nblk);
   const int tok_end = min(L, blk1 * BS);
 
-  int my_blk = lane < blk1 - blk0 ? table_id : 0;
-  const bool my_bad =
-      lane < blk1 - blk0 && (my_blk < 0 || my_blk >= p.num_blocks);
-  if (my_bad) my_blk = 0;
+  const int nb = blk1 - blk0;  // blocks of this partition, at most 128
+  int my_blk = lane < nb ? table_id : 0;
+  int my_blk2 = kWave + lane < nb ? table_id2 : 0;
+  const bool my_bad = (lane < nb && (my_blk < 0 || my_blk >= p.num_blocks)) ||
+                      (kWave + lane < nb && (my_blk2 < 0 || my_blk2 >= p.num_blocks));
+  if (my_blk < 0 || my_blk >= p.num_blocks) my_blk = 0;
+  if (my_blk2 < 0 || my_blk2 >= p.num_blocks) my_blk2 = 0;
   const bool bad = __any(my_bad);
+  // physical block of the partition's j-th block (j wave-uniform, < nb)
+  auto block_id = [&](int j) -> int {
+    return j < kWave ? __builtin_amdgcn_readlane(my_blk, j)
+                     : __builtin_amdgcn_readlane(my_blk2, j - kWave);
+  };
 
   float m = -INFINITY, lsum = 0.f;  // head hc; the 4 lanes of a head agree on m
   f4_t acc[VD];
@@ -412,7 +422,7 @@ __global__ __launch_bounds__(256) void decode_gqa_mfma_kernel(DecodeParams p) {
         // tile i lies in block b + 16i/BS, from its row 16i % BS
         const int bi = (16 * i) / BS;
         const bool in = b + bi < blk1;
-        const int phys = __builtin_amdgcn_readlane(my_blk, in ? b + bi - blk0 : 0);
+        const int phys = block_id(in ? b + bi - blk0 : 0);
         const size_t base = ((size_t)phys * p.num_kv_heads + kvh) * head_elems +
                             (size_t)((16 * i) % BS) * D;
         const _Float16 *kb = p.k_cache + base + (size_t)krow * D + 8 * kcol;
@@ -428,8 +438,8 @@ __global__ __launch_bounds__(256) void decode_gqa_mfma_kernel(DecodeParams p) {
         // block); V row 4g + r is in block B for g >= 2.
         const int bA = b + 2 * i, bB = bA + 1;
         const bool inA = bA < blk1, inB = bB < blk1;
-        const int phA = __builtin_amdgcn_readlane(my_blk, inA ? bA - blk0 : 0);
-        const int phB = __builtin_amdgcn_readlane(my_blk, inB ? bB - blk0 : 0);
+        const int phA = block_id(inA ? bA - blk0 : 0);
+        const int phB = block_id(inB ? bB - blk0 : 0);
         const size_t baseA = ((size_t)phA * p.num_kv_heads + kvh) * head_elems;
         const size_t baseB = ((size_t)phB * p.num_kv_heads + kvh) * head_elems;
 #pragma unroll
@@ -789,9 +799,9 @@ static hipError_t launch_heads(const DecodeParams &p, hipStream_t stream) {
 
 hipError_t launch_decode(const DecodeParams &p, int head_dim, int block_size,
                          hipStream_t stream) {
-  if (p.part_tokens <= 0 || p.part_tokens % block_size ||
-      p.part_tokens > kMaxPartBlocks * block_size || p.group <= 0 ||
-      p.num_q_heads % p.group)
+  if (p.part_tokens <= 0 || p.part_tokens % block_size || p.group <= 0 ||
+      p.num_q_heads % p.group ||
+      p.part_tokens > max_partition_blocks(p.group, block_size) * block_size)
     return hipErrorInvalidValue;
   if (head_dim == 128) {
     switch (block_size) {

@@ -63,6 +63,10 @@ SMALL_DECODE = [
     gpu_spec("d64_bs8_gqa16", 16, 1, 64, 8, EDGE_LENS, seed=24),
     # 4 query heads per KV head also run on the matrix cores
     gpu_spec("d64_bs8_gqa4", 8, 2, 64, 8, EDGE_LENS, seed=25),
+    # partitions of up to 128 blocks on the matrix cores: lengths around
+    # 64 and 128 blocks at block size 16
+    gpu_spec("d128_bs16_gqa8_long", 16, 2, 128, 16,
+             (1, 1023, 1024, 1025, 1040, 2047, 2048, 2049, 3000), seed=27),
 ]
 
 
@@ -167,11 +171,22 @@ def test_decode_config(name):
     check_decode(b, kc, vc, out)
 
 
+def max_partition(spec):
+    """Largest partition the decode takes: 128 blocks on the matrix-core
+    decode (4 or more query heads per workgroup, block size >= 8), else 64."""
+    G = spec.num_q_heads // spec.num_kv_heads
+    hpw = (16 if G % 16 == 0 and spec.block_size >= 8 else
+           8 if G % 8 == 0 else 4 if G % 4 == 0 else 2 if G % 2 == 0 else 1)
+    return (128 if hpw >= 4 and spec.block_size >= 8 else 64) * spec.block_size
+
+
 @pytest.mark.parametrize("spec", SMALL_DECODE, ids=lambda s: s.name)
-@pytest.mark.parametrize("part", [0, None, 64])
+@pytest.mark.parametrize("part", [0, None, 64, "max"])
 def test_decode_edge_lengths(spec, part):
-    # part None = one partition per block (the smallest split)
-    part = spec.block_size if part is None else part
+    # part None = one partition per block (the smallest split); "max" = the
+    # largest partition (block ids past the first 64 of a partition on the
+    # matrix-core decode)
+    part = spec.block_size if part is None else max_partition(spec) if part == "max" else part
     say("decode edges", spec.name, "partition", part)
     b = W.make_batch(spec, pad_rows=2)
     dev = DevBatch(b)
@@ -267,25 +282,32 @@ GQA16_BS8 = gpu_spec("d128_bs8_gqa16", 32, 2, 128, 8, (1, 17, 200, 700, 33, 64, 
 
 
 @pytest.mark.parametrize("spec,parts", [("llama_decode", (0, 1024)), (GQA_PERM, (0, 64)),
-                                        (GQA16_BS8, (0, 64))],
+                                        (GQA16_BS8, (0, 64, 1024))],
                          ids=["llama_decode", "gqa8_bs32", "gqa16_bs8"])
 def test_decode_bad_rows_are_nan_and_others_unaffected(spec, parts):
     # an out-of-pool block id, an empty sequence and a length beyond the
     # host bound poison their own rows only; on the vector-ALU kernel (MHA)
-    # and the matrix-core kernel (8 and 16 query heads per KV head)
+    # and the matrix-core kernel (8 and 16 query heads per KV head; at block
+    # size 8 with 1024-token partitions, also a bad id among a partition's
+    # blocks 64..127)
     b = W.make_batch(spec)
     dev = DevBatch(b)
     dev.append()
     bs = b.spec.block_size
     long_seqs = [s for s in range(b.num_dec) if b.lens_dec[s] > bs]
     s_blk = long_seqs[0]
-    s_zero, s_big = [s for s in range(b.num_dec) if s != s_blk][:2]
     tab = b.tables_dec.copy()
     tab[s_blk, 1] = b.spec.num_blocks + 7   # out-of-range block id
+    bad = [s_blk]
+    very_long = [s for s in range(b.num_dec) if b.lens_dec[s] > 70 * bs and s != s_blk]
+    if very_long:
+        tab[very_long[0], 70] = -3          # out of range, past the first 64 ids
+        bad.append(very_long[0])
+    s_zero, s_big = [s for s in range(b.num_dec) if s not in bad][:2]
     lens = b.lens_dec.copy()
     lens[s_zero] = 0                        # empty sequence
     lens[s_big] = dev.max_len_dec + 1       # beyond the host bound
-    bad = (s_blk, s_zero, s_big)
+    bad = tuple(bad) + (s_zero, s_big)
     others = [s for s in range(b.num_dec) if s not in bad]
     for part in parts:
         good = to_host(dev.decode(partition_size=part))
