@@ -25,11 +25,11 @@
 // * Softmax runs in base 2 with scale*log2(e) folded into the scores.  Tokens
 //   past the partition's end are removed by selecting (never by multiplying:
 //   tail slots may hold NaN).
-// * A sequence is cut into partitions of part_tokens (at most 64 blocks, so
-//   one VGPR holds the partition's block ids: lane j keeps entry j and a
-//   wave reads it with v_readlane, or, for blocks smaller than one
-//   wave-wide load, each lane fetches its token's entry with a lane
-//   permute).  One workgroup of 8 waves (fewer when a partition holds fewer
+// * A sequence is cut into partitions of part_tokens (at most 128 blocks, so
+//   two VGPRs hold the partition's block ids: lane j keeps entries j and
+//   64 + j and a wave reads them with v_readlane; for blocks smaller than
+//   one wave-wide load, at most 64 blocks, and each lane fetches its
+//   token's entry with a lane permute).  One workgroup of 8 waves (fewer when a partition holds fewer
 //   wave steps) takes one (partition, sequence, head group); waves take
 //   interleaved steps of whole blocks and are merged through LDS.
 // * With several partitions, each workgroup stores (max, sum, unnormalised
@@ -107,10 +107,13 @@ __global__ __launch_bounds__((64 * DecodeShape<D, BS>::NW)) void decode_kernel(D
   // from a table index clamped into the row, so the read needs no length)
   // and the query rows are loaded together, before any of them is used:
   // one memory latency before the first K/V load instead of three.
+  // Blocks that hold whole wave-wide loads allow partitions of up to 128
+  // blocks: lane j keeps entries j and 64 + j.
   const int part_blocks = p.part_tokens / BS;
   const int blk0 = part * part_blocks;  // < max_blocks_per_seq: part < num_parts
   const int32_t *trow = p.block_tables + (size_t)s * p.max_blocks_per_seq;
   const int table_id = trow[min(blk0 + lane, p.max_blocks_per_seq - 1)];
+  const int table_id2 = SUB ? 0 : trow[min(blk0 + kWave + lane, p.max_blocks_per_seq - 1)];
   const int L = p.seq_lens[s];
   const int col = lane % LPR;   // 16-byte column within a token row
   const int rrow = lane / LPR;  // token row within one wave-wide load
@@ -137,10 +140,13 @@ __global__ __launch_bounds__((64 * DecodeShape<D, BS>::NW)) void decode_kernel(D
 
   // An id outside the pool poisons the whole sequence (every wave sees the
   // same slice).
-  int my_blk = lane < blk1 - blk0 ? table_id : 0;
-  const bool my_bad =
-      lane < blk1 - blk0 && (my_blk < 0 || my_blk >= p.num_blocks);
-  if (my_bad) my_blk = 0;
+  const int nb = blk1 - blk0;  // blocks of this partition
+  int my_blk = lane < nb ? table_id : 0;
+  int my_blk2 = kWave + lane < nb ? table_id2 : 0;
+  const bool my_bad = (lane < nb && (my_blk < 0 || my_blk >= p.num_blocks)) ||
+                      (kWave + lane < nb && (my_blk2 < 0 || my_blk2 >= p.num_blocks));
+  if (my_blk < 0 || my_blk >= p.num_blocks) my_blk = 0;
+  if (my_blk2 < 0 || my_blk2 >= p.num_blocks) my_blk2 = 0;
   const bool bad = __any(my_bad);
 
   float m[GH], lsum[GH], acc[GH][8];
@@ -160,8 +166,10 @@ __global__ __launch_bounds__((64 * DecodeShape<D, BS>::NW)) void decode_kernel(D
 #pragma unroll
       for (int c = 0; c < BPS; ++c) {
         const int bb = b + c;
+        const int j = bb < blk1 ? bb - blk0 : 0;  // wave-uniform, < nb
+        const int phys = j < kWave ? __builtin_amdgcn_readlane(my_blk, j)
+                                   : __builtin_amdgcn_readlane(my_blk2, j - kWave);
         const bool in = bb < blk1;
-        const int phys = __builtin_amdgcn_readlane(my_blk, in ? bb - blk0 : 0);
         const size_t base =
             ((size_t)phys * p.num_kv_heads + kvh) * head_elems + rrow * D + col * 8;
 #pragma unroll

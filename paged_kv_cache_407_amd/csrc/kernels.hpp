@@ -71,10 +71,11 @@ struct CopyParams {
 hipError_t launch_copy_blocks(const CopyParams &p, hipStream_t stream);
 // D in {64,128}, BS in {1,8,16,32}; returns hipErrorInvalidValue otherwise.
 // part_tokens must be a multiple of BS and at most max_partition_blocks() *
-// BS: the vector-ALU decode keeps a partition's block ids one per lane (64
-// blocks), the matrix-core decode two per lane (128 blocks).
+// BS: a wave keeps a partition's block ids two per lane (128 blocks), or
+// one per lane (64 blocks) when blocks are smaller than a wave-wide load and
+// each lane fetches its own token's id by a lane permute (block size 1).
 constexpr int kMaxPartBlocks = 64;
-constexpr int kMaxPartBlocksMfma = 128;
+constexpr int kMaxPartBlocksWide = 128;
 // Query heads one decode workgroup serves: the largest of 8, 4, 2, 1 that
 // divides the group of query heads sharing one KV head, or 16 when 16
 // divides it and the matrix-core kernel serves the block size (>= 8).
@@ -88,7 +89,8 @@ inline bool decode_on_mfma(int group, int block_size) {
   return heads_per_workgroup(group, block_size) >= 4 && block_size >= 8;
 }
 inline int max_partition_blocks(int group, int block_size) {
-  return decode_on_mfma(group, block_size) ? kMaxPartBlocksMfma : kMaxPartBlocks;
+  (void)group;
+  return block_size >= 8 ? kMaxPartBlocksWide : kMaxPartBlocks;
 }
 hipError_t launch_decode(const DecodeParams &p, int head_dim, int block_size,
                          hipStream_t stream);

@@ -172,20 +172,16 @@ def test_decode_config(name):
 
 
 def max_partition(spec):
-    """Largest partition the decode takes: 128 blocks on the matrix-core
-    decode (4 or more query heads per workgroup, block size >= 8), else 64."""
-    G = spec.num_q_heads // spec.num_kv_heads
-    hpw = (16 if G % 16 == 0 and spec.block_size >= 8 else
-           8 if G % 8 == 0 else 4 if G % 4 == 0 else 2 if G % 2 == 0 else 1)
-    return (128 if hpw >= 4 and spec.block_size >= 8 else 64) * spec.block_size
+    """Largest partition the decode takes: 128 blocks (two block ids per
+    lane), 64 at block size 1."""
+    return (128 if spec.block_size >= 8 else 64) * spec.block_size
 
 
 @pytest.mark.parametrize("spec", SMALL_DECODE, ids=lambda s: s.name)
 @pytest.mark.parametrize("part", [0, None, 64, "max"])
 def test_decode_edge_lengths(spec, part):
     # part None = one partition per block (the smallest split); "max" = the
-    # largest partition (block ids past the first 64 of a partition on the
-    # matrix-core decode)
+    # largest partition (block ids past the first 64 of a partition)
     part = spec.block_size if part is None else max_partition(spec) if part == "max" else part
     say("decode edges", spec.name, "partition", part)
     b = W.make_batch(spec, pad_rows=2)
