@@ -562,13 +562,13 @@ def main():
     log("library", pkv.LIB_PATH, "device", torch.cuda.get_device_name(dev))
     headline = args.workload or HEADLINE
     if args.block_size_sweep:
-        block_size_sweep(args, dev, headline)
+        block_size_sweep(args, dev, args.workload or "llama_decode")
         return
     if args.prefill_sweep:
         prefill_sweep(args, dev)
         return
     if args.swap_bench:
-        swap_bench(args, dev, headline)
+        swap_bench(args, dev, args.workload or "llama_decode")
         return
     if args.serve:
         serve_bench(args, dev, args.workload or "llama_decode")
