@@ -614,6 +614,51 @@ def test_decode_graph_replays_match_eager(name):
         assert np.array_equal(got.view(np.uint32), eager.view(np.uint32)), i
 
 
+def test_prefill_split_graph_replays_match_eager():
+    # the split prefill (parts into the workspace, then the merge kernel)
+    # captured in a HIP graph: every replay, with other prefill work on the
+    # same workspace in between, matches the eager call bit for bit
+    spec = split_spec(128, 16, 2, 1, seed=91)
+    b = W.make_batch(spec, lens_override={"prefix": SPLIT_PREFIXES})
+    dev = DevBatch(b)
+    dev.append()
+    T, Hq, D = b.q_pf.shape
+    maxl = int(b.lens_pf.max())
+    need = pkv.prefill_workspace_size(len(SPLIT_PREFIXES), T, SPLIT_CHUNK, Hq, D, maxl)
+    loose = spec.max_blocks_per_seq * 16     # a looser bound splits differently
+    need2 = pkv.prefill_workspace_size(len(SPLIT_PREFIXES), T, SPLIT_CHUNK, Hq, D, loose)
+    assert need > 0 and need2 > 0
+    ws = torch.zeros(max(need, need2), dtype=torch.uint8, device="cuda")
+    out = torch.empty((T, Hq, D), dtype=torch.float32, device="cuda")
+
+    def run():
+        pkv.paged_attention_prefill(dev.q_pf, dev.cu, dev.k_cache, dev.v_cache, dev.tables_pf,
+                                    dev.lens_pf, max_q_len=SPLIT_CHUNK, max_seq_len=maxl,
+                                    scale=b.scale, out=out, workspace=ws)
+
+    run()
+    torch.cuda.synchronize()
+    eager = to_host(out).copy()
+    kc, vc = check_append(b, dev)
+    check_prefill(b, kc, vc, eager)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for i in range(4):
+        out.fill_(float("nan"))
+        split_call(b, dev, loose, workspace=ws)   # another split on the same workspace
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host(out).view(np.uint32), eager.view(np.uint32)), i
+
+
 # ------------------------------------------------------- host block manager
 def test_block_manager_drives_append_and_decode():
     """Block tables and slot mappings from the host block manager drive the

@@ -70,3 +70,42 @@ def test_noalloc_refuses_partials_beyond_its_scratch():
                                            scale=b.scale, partition_size=16)
     torch.cuda.synchronize()
     assert np.isnan(to_host(out)).all()
+
+
+def test_noalloc_decode_under_graph_capture_replays():
+    # the motivating caller: a HIP graph holding the decode (split, so the
+    # partials live in the library's scratch); every replay, with eager work
+    # of another shape on the same scratch in between, matches the eager call
+    b = W.make_batch("llama_decode")
+    dev = DevBatch(b)
+    dev.append()
+    part = 64
+    out = torch.empty(tuple(b.q_dec.shape), dtype=torch.float32, device="cuda")
+
+    def run():
+        pkv.paged_attention_decode_noalloc(dev.q_dec, dev.k_cache, dev.v_cache, dev.tables_dec,
+                                           dev.lens_dec, out, max_seq_len=dev.max_len_dec,
+                                           scale=b.scale, partition_size=part)
+
+    run()
+    torch.cuda.synchronize()
+    eager = to_host(out).copy()
+    other = DevBatch(W.make_batch("tiny"))
+    other.append()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for i in range(4):
+        out.fill_(float("nan"))
+        _noalloc(other, 16)            # another call on the same scratch
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = to_host(out)
+        assert np.array_equal(got.view(np.uint32), eager.view(np.uint32)), i
