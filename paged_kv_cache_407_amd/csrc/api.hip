@@ -15,12 +15,15 @@ using namespace pkv;
 namespace {
 
 // Default split: the largest partition (4096, 2048, 1024, 512 or 256
-// tokens, at most 64 blocks -- 128 on the matrix-core decode -- so 1024 at
-// block size 16 for MHA) that still gives at least kTargetWorkgroups decode
-// workgroups (4 per CU on the chip's 256 CUs), so long sequences run few,
-// long workgroups, a batch that fills the chip is not split (no merge
-// launch), and short batches are cut until they fill it.
+// tokens, at most 256 blocks -- 64 at block size 1) that still gives at
+// least kTargetWorkgroups decode workgroups on the vector-ALU decode (4 per
+// CU on the chip's 256 CUs) or kTargetWorkgroupsMfma on the matrix-core
+// decode (2 per CU; its workgroups are shorter-lived per token and all of
+// them stay resident), so long sequences run few, long workgroups, a batch
+// that fills the chip is not split (no merge launch), and short batches are
+// cut until they fill it.
 constexpr int kTargetWorkgroups = 1024;
+constexpr int kTargetWorkgroupsMfma = 512;
 constexpr int kPartitionChoices[] = {4096, 2048, 1024, 512, 256};
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
@@ -56,10 +59,12 @@ int32_t partition_tokens(int32_t num_seqs, int32_t num_q_heads,
   int64_t rows = (int64_t)(num_seqs > 0 ? num_seqs : 1) * (num_q_heads > 0 ? num_q_heads : 1);
   if (num_q_heads > 0 && num_kv_heads > 0 && num_q_heads % num_kv_heads == 0)
     rows /= heads_per_workgroup(num_q_heads / num_kv_heads, block_size);
+  const int64_t target =
+      decode_on_mfma(group, block_size) ? kTargetWorkgroupsMfma : kTargetWorkgroups;
   int64_t part = 0;
   for (int choice : kPartitionChoices) {
     part = std::min<int64_t>(round_up(choice, block_size), cap);
-    if (rows * ((max_seq_len + part - 1) / part) >= kTargetWorkgroups) break;
+    if (rows * ((max_seq_len + part - 1) / part) >= target) break;
   }
   if (max_seq_len <= part) part = round_up(max_seq_len, block_size);
   return (int32_t)part;

@@ -124,6 +124,39 @@ __device__ __forceinline__ float dot8(h8_t a, h8_t b, float acc) {
   return acc;
 }
 
+// Block ids of one decode partition of up to 64 * N blocks, N per lane:
+// lane l keeps entries l, 64 + l, ..., read back wave-uniformly with
+// v_readlane.  issue() loads them (clamped, always in bounds) before the
+// partition's length is known; settle() then replaces entries outside the
+// pool with 0 and reports whether a live entry (index < nb) was one.
+template <int N>
+struct PartitionIds {
+  int v[N];
+  __device__ __forceinline__ void issue(const int32_t *trow, int blk0, int max_blocks,
+                                        int lane) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = trow[min(blk0 + kWave * i + lane, max_blocks - 1)];
+  }
+  __device__ __forceinline__ bool settle(int nb, int num_blocks, int lane) {
+    bool bad = false;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const bool out = v[i] < 0 || v[i] >= num_blocks;
+      bad |= kWave * i + lane < nb && out;
+      if (out || kWave * i + lane >= nb) v[i] = 0;
+    }
+    return bad;
+  }
+  // entry j of the partition, j wave-uniform and < 64 * N
+  __device__ __forceinline__ int get(int j) const {
+    int r = __builtin_amdgcn_readlane(v[0], j & (kWave - 1));
+#pragma unroll
+    for (int i = 1; i < N; ++i)
+      if (j >= kWave * i) r = __builtin_amdgcn_readlane(v[i], j & (kWave - 1));
+    return r;
+  }
+};
+
 // v_mfma_f32_16x16x32_f16: D(16x16) = A(16x32) B(32x16) + C.  Lane l
 // supplies row l%16 of A and column l%16 of B, each as 8 fp16 values of the
 // contraction index (group l/16); lane l receives D rows 4*(l/16)+r, r<4,

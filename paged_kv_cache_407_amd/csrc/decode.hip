@@ -25,10 +25,10 @@
 // * Softmax runs in base 2 with scale*log2(e) folded into the scores.  Tokens
 //   past the partition's end are removed by selecting (never by multiplying:
 //   tail slots may hold NaN).
-// * A sequence is cut into partitions of part_tokens (at most 128 blocks, so
-//   two VGPRs hold the partition's block ids: lane j keeps entries j and
-//   64 + j and a wave reads them with v_readlane; for blocks smaller than
-//   one wave-wide load, at most 64 blocks, and each lane fetches its
+// * A sequence is cut into partitions of part_tokens (at most 256 blocks, so
+//   four VGPRs hold the partition's block ids: lane j keeps entries j,
+//   64 + j, ... and a wave reads them with v_readlane; for blocks smaller
+//   than one wave-wide load, at most 64 blocks, and each lane fetches its
 //   token's entry with a lane permute).  One workgroup of 8 waves (fewer when a partition holds fewer
 //   wave steps) takes one (partition, sequence, head group); waves take
 //   interleaved steps of whole blocks and are merged through LDS.
@@ -107,13 +107,14 @@ __global__ __launch_bounds__((64 * DecodeShape<D, BS>::NW)) void decode_kernel(D
   // from a table index clamped into the row, so the read needs no length)
   // and the query rows are loaded together, before any of them is used:
   // one memory latency before the first K/V load instead of three.
-  // Blocks that hold whole wave-wide loads allow partitions of up to 128
-  // blocks: lane j keeps entries j and 64 + j.
+  // Blocks that hold whole wave-wide loads allow partitions of up to 256
+  // blocks (4 ids per lane); smaller blocks 64 (one id per lane, fetched
+  // by the lanes that need it).
   const int part_blocks = p.part_tokens / BS;
   const int blk0 = part * part_blocks;  // < max_blocks_per_seq: part < num_parts
   const int32_t *trow = p.block_tables + (size_t)s * p.max_blocks_per_seq;
-  const int table_id = trow[min(blk0 + lane, p.max_blocks_per_seq - 1)];
-  const int table_id2 = SUB ? 0 : trow[min(blk0 + kWave + lane, p.max_blocks_per_seq - 1)];
+  PartitionIds<SUB ? 1 : kIdsPerLane> ids;
+  ids.issue(trow, blk0, p.max_blocks_per_seq, lane);
   const int L = p.seq_lens[s];
   const int col = lane % LPR;   // 16-byte column within a token row
   const int rrow = lane / LPR;  // token row within one wave-wide load
@@ -140,14 +141,7 @@ __global__ __launch_bounds__((64 * DecodeShape<D, BS>::NW)) void decode_kernel(D
 
   // An id outside the pool poisons the whole sequence (every wave sees the
   // same slice).
-  const int nb = blk1 - blk0;  // blocks of this partition
-  int my_blk = lane < nb ? table_id : 0;
-  int my_blk2 = kWave + lane < nb ? table_id2 : 0;
-  const bool my_bad = (lane < nb && (my_blk < 0 || my_blk >= p.num_blocks)) ||
-                      (kWave + lane < nb && (my_blk2 < 0 || my_blk2 >= p.num_blocks));
-  if (my_blk < 0 || my_blk >= p.num_blocks) my_blk = 0;
-  if (my_blk2 < 0 || my_blk2 >= p.num_blocks) my_blk2 = 0;
-  const bool bad = __any(my_bad);
+  const bool bad = __any(ids.settle(blk1 - blk0, p.num_blocks, lane));
 
   float m[GH], lsum[GH], acc[GH][8];
 #pragma unroll
@@ -166,10 +160,8 @@ __global__ __launch_bounds__((64 * DecodeShape<D, BS>::NW)) void decode_kernel(D
 #pragma unroll
       for (int c = 0; c < BPS; ++c) {
         const int bb = b + c;
-        const int j = bb < blk1 ? bb - blk0 : 0;  // wave-uniform, < nb
-        const int phys = j < kWave ? __builtin_amdgcn_readlane(my_blk, j)
-                                   : __builtin_amdgcn_readlane(my_blk2, j - kWave);
         const bool in = bb < blk1;
+        const int phys = ids.get(in ? bb - blk0 : 0);
         const size_t base =
             ((size_t)phys * p.num_kv_heads + kvh) * head_elems + rrow * D + col * 8;
 #pragma unroll
@@ -190,7 +182,7 @@ __global__ __launch_bounds__((64 * DecodeShape<D, BS>::NW)) void decode_kernel(D
       for (int i = 0; i < NL; ++i) {
         const int tok = b * BS + i * RPL + rrow;
         const int bl = tok / BS - blk0;
-        const int phys = __shfl(my_blk, bl < blk1 - blk0 ? bl : 0, kWave);
+        const int phys = __shfl(ids.v[0], bl < blk1 - blk0 ? bl : 0, kWave);
         const size_t off = ((size_t)phys * p.num_kv_heads + kvh) * head_elems +
                            (size_t)(tok % BS) * D + col * 8;
         kr[i] = ld16_nt(p.k_cache + off);
@@ -355,12 +347,12 @@ __global__ __launch_bounds__(256) void decode_gqa_mfma_kernel(DecodeParams p) {
   // Length, block ids (clamped table index) and query rows are loaded
   // together, as in decode_kernel.  Q^T operand: head hc, zero for hc >= GH
   // (the address is clamped into the head group).
-  // A partition holds up to 128 blocks: lane j keeps entries j and 64 + j.
+  // A partition holds up to 256 blocks, 4 ids per lane.
   const int part_blocks = p.part_tokens / BS;
   const int blk0 = part * part_blocks;
   const int32_t *trow = p.block_tables + (size_t)s * p.max_blocks_per_seq;
-  const int table_id = trow[min(blk0 + lane, p.max_blocks_per_seq - 1)];
-  const int table_id2 = trow[min(blk0 + kWave + lane, p.max_blocks_per_seq - 1)];
+  PartitionIds<kIdsPerLane> ids;
+  ids.issue(trow, blk0, p.max_blocks_per_seq, lane);
   const int L = p.seq_lens[s];
   const uint4 zero = make_uint4(0, 0, 0, 0);
   h8_t qv[KQ];
@@ -384,19 +376,9 @@ __global__ __launch_bounds__(256) void decode_gqa_mfma_kernel(DecodeParams p) {
   const int blk1 = min(blk0 + part_blocks, nblk);
   const int tok_end = min(L, blk1 * BS);
 
-  const int nb = blk1 - blk0;  // blocks of this partition, at most 128
-  int my_blk = lane < nb ? table_id : 0;
-  int my_blk2 = kWave + lane < nb ? table_id2 : 0;
-  const bool my_bad = (lane < nb && (my_blk < 0 || my_blk >= p.num_blocks)) ||
-                      (kWave + lane < nb && (my_blk2 < 0 || my_blk2 >= p.num_blocks));
-  if (my_blk < 0 || my_blk >= p.num_blocks) my_blk = 0;
-  if (my_blk2 < 0 || my_blk2 >= p.num_blocks) my_blk2 = 0;
-  const bool bad = __any(my_bad);
+  const bool bad = __any(ids.settle(blk1 - blk0, p.num_blocks, lane));
   // physical block of the partition's j-th block (j wave-uniform, < nb)
-  auto block_id = [&](int j) -> int {
-    return j < kWave ? __builtin_amdgcn_readlane(my_blk, j)
-                     : __builtin_amdgcn_readlane(my_blk2, j - kWave);
-  };
+  auto block_id = [&](int j) -> int { return ids.get(j); };
 
   float m = -INFINITY, lsum = 0.f;  // head hc; the 4 lanes of a head agree on m
   f4_t acc[VD];

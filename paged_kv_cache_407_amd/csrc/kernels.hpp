@@ -71,11 +71,13 @@ struct CopyParams {
 hipError_t launch_copy_blocks(const CopyParams &p, hipStream_t stream);
 // D in {64,128}, BS in {1,8,16,32}; returns hipErrorInvalidValue otherwise.
 // part_tokens must be a multiple of BS and at most max_partition_blocks() *
-// BS: a wave keeps a partition's block ids two per lane (128 blocks), or
-// one per lane (64 blocks) when blocks are smaller than a wave-wide load and
-// each lane fetches its own token's id by a lane permute (block size 1).
+// BS: a wave keeps a partition's block ids kIdsPerLane per lane (256
+// blocks), or one per lane (64 blocks) when blocks are smaller than a
+// wave-wide load and each lane fetches its own token's id by a lane permute
+// (block size 1).
 constexpr int kMaxPartBlocks = 64;
-constexpr int kMaxPartBlocksWide = 128;
+constexpr int kIdsPerLane = 4;
+constexpr int kMaxPartBlocksWide = 64 * kIdsPerLane;
 // Query heads one decode workgroup serves: the largest of 8, 4, 2, 1 that
 // divides the group of query heads sharing one KV head, or 16 when 16
 // divides it and the matrix-core kernel serves the block size (>= 8).

@@ -59,26 +59,30 @@ def test_partition_and_workspace_policy():
     # the largest of 2048 / 1024 / 512 / 256 tokens (at most 64 blocks) that
     # still gives at least 1024 workgroups; a sequence that fits one
     # partition is not split
-    assert pkv.decode_partition_size(8, 32, 32, 128, 16, 32768) == 2048      # 8 x 32K
+    assert pkv.decode_partition_size(8, 32, 32, 128, 16, 32768) == 4096      # 8 x 32K
     assert pkv.decode_partition_size(60, 32, 32, 128, 16, 2031) == 2032      # mixed step
     assert pkv.decode_partition_size(32, 32, 32, 128, 16, 1017) == 1024      # batch 32
     assert pkv.decode_workspace_size(32, 32, 32, 128, 16, 1017) == 0
     assert pkv.decode_partition_size(4, 32, 32, 128, 16, 1017) == 256        # batch 4
     assert pkv.decode_partition_size(8, 32, 32, 128, 16, 2048) == 512        # batch 8
-    # the GQA 64/8 batch of up to 4096 tokens at block size 32 is not split
+    # the matrix-core decode aims at 512 workgroups: the GQA 64/8 batch of up
+    # to 4096 tokens at block size 32 and the 32/8 and 128/8 batches of up to
+    # 3072 tokens at block size 16 are not split
     assert pkv.decode_partition_size(256, 64, 8, 128, 32, 4096) == 4096      # GQA 64/8
     assert pkv.decode_workspace_size(256, 64, 8, 128, 32, 4096) == 0
-    assert pkv.decode_partition_size(64, 32, 8, 128, 16, 3072) == 2048       # GQA 32/8
+    assert pkv.decode_partition_size(64, 32, 8, 128, 16, 3072) == 3072       # GQA 32/8
+    assert pkv.decode_partition_size(64, 128, 8, 128, 16, 3072) == 3072      # GQA 128/8
+    assert pkv.decode_workspace_size(64, 128, 8, 128, 16, 3072) == 0
     assert pkv.decode_partition_size(8, 8, 1, 64, 1, 4096, 128) == 0         # block size 1
     ws = pkv.decode_workspace_size(8, 32, 32, 128, 16, 32768)
-    rows = 8 * 32 * 16
+    rows = 8 * 32 * 8
     assert ws >= rows * (128 + 2) * 4
     # a requested size must be a multiple of the block size
     assert pkv.decode_partition_size(8, 32, 32, 128, 16, 1000, 24) == 0
     assert pkv.decode_partition_size(8, 32, 32, 128, 16, 1000, 32) == 32
-    # at most 128 blocks per partition (64 at block size 1)
-    assert pkv.decode_partition_size(8, 32, 32, 128, 16, 4096, 2048) == 2048
-    assert pkv.decode_partition_size(8, 32, 32, 128, 16, 4096, 2064) == 0
+    # at most 256 blocks per partition (64 at block size 1)
+    assert pkv.decode_partition_size(8, 32, 32, 128, 16, 8192, 4096) == 4096
+    assert pkv.decode_partition_size(8, 32, 32, 128, 16, 8192, 4112) == 0
     assert pkv.decode_partition_size(8, 32, 32, 128, 1, 4096, 64) == 64
     assert pkv.decode_partition_size(8, 32, 32, 128, 1, 4096, 65) == 0
     assert pkv.decode_partition_size(8, 32, 32, 128, 32, 4096, 2048) == 2048

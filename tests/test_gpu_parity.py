@@ -63,10 +63,13 @@ SMALL_DECODE = [
     gpu_spec("d64_bs8_gqa16", 16, 1, 64, 8, EDGE_LENS, seed=24),
     # 4 query heads per KV head also run on the matrix cores
     gpu_spec("d64_bs8_gqa4", 8, 2, 64, 8, EDGE_LENS, seed=25),
-    # partitions of up to 128 blocks on the matrix cores: lengths around
-    # 64 and 128 blocks at block size 16
+    # partitions of up to 256 blocks: lengths around 64, 128 and 192 blocks
+    # at block size 16 (matrix cores) and up to 256 blocks at block size 8
+    # (vector ALUs)
     gpu_spec("d128_bs16_gqa8_long", 16, 2, 128, 16,
-             (1, 1023, 1024, 1025, 1040, 2047, 2048, 2049, 3000), seed=27),
+             (1, 1023, 1024, 1025, 1040, 2047, 2048, 2049, 3000, 3073, 4096), seed=27),
+    gpu_spec("d64_bs8_mha_long", 4, 4, 64, 8, (1, 511, 512, 513, 1024, 1536, 2000, 2048),
+             seed=28),
 ]
 
 
@@ -172,9 +175,9 @@ def test_decode_config(name):
 
 
 def max_partition(spec):
-    """Largest partition the decode takes: 128 blocks (two block ids per
+    """Largest partition the decode takes: 256 blocks (four block ids per
     lane), 64 at block size 1."""
-    return (128 if spec.block_size >= 8 else 64) * spec.block_size
+    return (256 if spec.block_size >= 8 else 64) * spec.block_size
 
 
 @pytest.mark.parametrize("spec", SMALL_DECODE, ids=lambda s: s.name)
@@ -277,9 +280,13 @@ GQA16_BS8 = gpu_spec("d128_bs8_gqa16", 32, 2, 128, 8, (1, 17, 200, 700, 33, 64, 
                      seed=26)
 
 
+MHA_BS8_LONG = gpu_spec("mha_bs8_long", 4, 4, 64, 8, (1, 600, 1000, 1700, 2000, 2048), seed=29)
+
+
 @pytest.mark.parametrize("spec,parts", [("llama_decode", (0, 1024)), (GQA_PERM, (0, 64)),
-                                        (GQA16_BS8, (0, 64, 1024))],
-                         ids=["llama_decode", "gqa8_bs32", "gqa16_bs8"])
+                                        (GQA16_BS8, (0, 64, 1024)),
+                                        (MHA_BS8_LONG, (0, 2048))],
+                         ids=["llama_decode", "gqa8_bs32", "gqa16_bs8", "mha_bs8_long"])
 def test_decode_bad_rows_are_nan_and_others_unaffected(spec, parts):
     # an out-of-pool block id, an empty sequence and a length beyond the
     # host bound poison their own rows only; on the vector-ALU kernel (MHA)
@@ -295,10 +302,13 @@ def test_decode_bad_rows_are_nan_and_others_unaffected(spec, parts):
     tab = b.tables_dec.copy()
     tab[s_blk, 1] = b.spec.num_blocks + 7   # out-of-range block id
     bad = [s_blk]
-    very_long = [s for s in range(b.num_dec) if b.lens_dec[s] > 70 * bs and s != s_blk]
-    if very_long:
-        tab[very_long[0], 70] = -3          # out of range, past the first 64 ids
-        bad.append(very_long[0])
+    # out-of-range ids past the first 64 and past the first 192 of a
+    # partition (second and fourth id register), in other sequences
+    for j in (70, 200):
+        cand = [s for s in range(b.num_dec) if b.lens_dec[s] > (j + 1) * bs and s not in bad]
+        if cand:
+            tab[cand[0], j] = -3
+            bad.append(cand[0])
     s_zero, s_big = [s for s in range(b.num_dec) if s not in bad][:2]
     lens = b.lens_dec.copy()
     lens[s_zero] = 0                        # empty sequence

@@ -31,7 +31,7 @@ def _noalloc(dev, part):
 
 
 @pytest.mark.parametrize("first,second", [(("llama_decode", 64), ("tiny", 16)),
-                                          (("gqa_shared", 2048), ("gqa4", 0))],
+                                          (("gqa_shared", 2048), ("gqa4", 1024))],
                          ids=["mha", "gqa"])
 def test_noalloc_matches_workspace_entry_on_consecutive_calls(first, second):
     for name, part in (first, second):
