@@ -108,8 +108,9 @@ int32_t pkv_decode_partition_size(int32_t num_seqs, int32_t num_q_heads,
  *   max_seq_len  : host-side upper bound of seq_lens (sizes the split)
  *   scale        : score scale, finite and > 0, normally 1/sqrt(head_dim)
  *   partition_size : tokens per split-sequence partition, a positive
- *                  multiple of block_size and at most 64 * block_size;
- *                  0 = library's choice.  Partitions are merged with the
+ *                  multiple of block_size and at most 256 * block_size
+ *                  (64 * block_size when block_size < 8), else
+ *                  PKV_ERR_INVALID; 0 = library's choice.  Partitions are merged with the
  *                  log-sum-exp identity of the running max / sum recurrence
  *                  (a second kernel, enqueued by the same call).
  *   seq_order    : host, [num_seqs] int32, may be NULL: the order in which

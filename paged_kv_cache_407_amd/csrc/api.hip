@@ -43,8 +43,8 @@ bool supported_prefill(int32_t head_dim, int32_t block_size) {
 int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 
 // Tokens per partition; 0 when the arguments are invalid.  A partition
-// holds at most max_partition_blocks() blocks (one or two VGPRs of block
-// ids per wave).
+// holds at most max_partition_blocks() blocks (four VGPRs of block ids per
+// wave; one at block size 1).
 int32_t partition_tokens(int32_t num_seqs, int32_t num_q_heads,
                          int32_t num_kv_heads, int32_t block_size,
                          int32_t max_seq_len, int32_t requested) {
@@ -52,7 +52,7 @@ int32_t partition_tokens(int32_t num_seqs, int32_t num_q_heads,
   const int group = (num_q_heads > 0 && num_kv_heads > 0 && num_q_heads % num_kv_heads == 0)
                         ? num_q_heads / num_kv_heads
                         : 1;
-  const int64_t cap = (int64_t)max_partition_blocks(group, block_size) * block_size;
+  const int64_t cap = (int64_t)max_partition_blocks(block_size) * block_size;
   if (requested > 0)
     return (requested % block_size || requested > cap) ? 0 : requested;
   if (requested < 0) return 0;

@@ -791,7 +791,7 @@ hipError_t launch_decode(const DecodeParams &p, int head_dim, int block_size,
                          hipStream_t stream) {
   if (p.part_tokens <= 0 || p.part_tokens % block_size || p.group <= 0 ||
       p.num_q_heads % p.group ||
-      p.part_tokens > max_partition_blocks(p.group, block_size) * block_size)
+      p.part_tokens > max_partition_blocks(block_size) * block_size)
     return hipErrorInvalidValue;
   if (head_dim == 128) {
     switch (block_size) {

@@ -90,8 +90,7 @@ inline int heads_per_workgroup(int group, int block_size) {
 inline bool decode_on_mfma(int group, int block_size) {
   return heads_per_workgroup(group, block_size) >= 4 && block_size >= 8;
 }
-inline int max_partition_blocks(int group, int block_size) {
-  (void)group;
+inline int max_partition_blocks(int block_size) {
   return block_size >= 8 ? kMaxPartBlocksWide : kMaxPartBlocks;
 }
 hipError_t launch_decode(const DecodeParams &p, int head_dim, int block_size,
