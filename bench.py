@@ -22,7 +22,9 @@ synchronisations; ms_per_step is the event time / K.
 
 Roofline of the dominant call (decode): algorithmic bytes per launch (KV rows
 read once -- each physical (block, offset) once -- plus queries and outputs)
-divided by its launch duration.  Durations come from HIP events on the
+divided by its launch duration, against the 8 TB/s datasheet peak and, as
+frac_of_stream_read, against a plain sequential read of 4 GiB timed the same
+way on the same device (``stream_read``).  Durations come from HIP events on the
 launch stream around batches of back-to-back calls (a spin kernel keeps the
 GPU ahead of the host), divided by the batch size; the median over batches
 is reported with its p10 / p90.  This does not depend on --steps.
@@ -327,6 +329,50 @@ def launch_stats(call, batches=TIMING_BATCHES, per_batch=TIMING_CALLS) -> dict:
             "calls": batches * per_batch, "batches": batches}
 
 
+STREAM_BYTES = 4 << 30
+STREAM_GRIDS = (8192, 32768, 65536, 131072)
+BENCH_LIB = os.path.join(ROOT, "paged_kv_cache_407_amd", "libpkv_bench.so")
+
+
+def stream_read_reference(dev) -> dict:
+    """What a plain sequential read of HBM reaches on this device: the
+    streaming-read kernel of libpkv_bench.so (16-byte nontemporal loads, the
+    decode's load form; two streams, the halves of a 4 GiB buffer), timed like the decode
+    (launch_stats), best of a few grid sizes.  The decode's achieved
+    bandwidth is also reported as a fraction of it."""
+    import ctypes
+    import torch
+    if not os.path.exists(BENCH_LIB):
+        raise SystemExit(f"{BENCH_LIB} is missing: run __graft_entry__.build() first")
+    lib = ctypes.CDLL(BENCH_LIB)
+    fn = lib.pkvb_stream_read
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int32,
+                   ctypes.c_void_p]
+    buf = torch.ones(STREAM_BYTES // 4, dtype=torch.int32, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    best = None
+    for grid in STREAM_GRIDS:
+        def call(_i, grid=grid):
+            rc = fn(buf.data_ptr(), STREAM_BYTES, sink.data_ptr(), grid, stream)
+            if rc:
+                raise RuntimeError(f"pkvb_stream_read failed: hip error {rc}")
+        call(0)
+        torch.cuda.synchronize()
+        st = launch_stats(call, batches=5, per_batch=5)
+        gbs = STREAM_BYTES / (st["us_median"] * 1e-6) / 1e9
+        log(f"stream read, {grid} workgroups: {st['us_median']} us, {gbs:.1f} GB/s")
+        if best is None or gbs > best["GBps"]:
+            best = {"GBps": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+                    "bytes": STREAM_BYTES, "workgroups": grid, "us_median": st["us_median"],
+                    "kernel": "stream_read_kernel (libpkv_bench.so)"}
+    del buf, sink
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return best
+
+
 def to_device(a, dev):
     import torch
     a = np.ascontiguousarray(a)
@@ -600,6 +646,11 @@ def main():
         line["per_config"] = {}
         for name in extra:
             line["per_config"][name] = measure(name, args, dev, cpu and cpu / 3)
+    sr = stream_read_reference(dev)
+    line["stream_read"] = sr
+    for r in [line, *line.get("per_config", {}).values()]:
+        if "roofline" in r:
+            r["roofline"]["frac_of_stream_read"] = round(r["roofline"]["achieved"] / sr["GBps"], 4)
     print(json.dumps(line), flush=True)
 
 

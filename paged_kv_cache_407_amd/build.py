@@ -71,6 +71,26 @@ def build(verbose: bool = False, jobs: int | None = None) -> Path:
     return LIB
 
 
+# Measurement helper, apart from the library: a streaming-read kernel that
+# bench.py times as the reference for a plain sequential read of HBM.
+BENCH_SRC = CSRC / "bench" / "stream_read.hip"
+BENCH_LIB = HERE / "libpkv_bench.so"
+
+
+def build_bench(verbose: bool = False) -> Path:
+    tmp = BENCH_LIB.with_suffix(".so.tmp")
+    cmd = [hipcc(), *FLAGS, "-shared", "-o", str(tmp), str(BENCH_SRC)]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode:
+        noise = "is not a recognized feature for this target"
+        err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)
+        raise RuntimeError(f"hipcc failed on {BENCH_SRC.name}:\n{err}")
+    os.replace(tmp, BENCH_LIB)
+    return BENCH_LIB
+
+
 # Host-only build of the plain host sources with AddressSanitizer and
 # UndefinedBehaviorSanitizer (g++, no device code): the block manager, the
 # scheduler, the precondition checks and the status strings.  The binding
@@ -94,3 +114,4 @@ def build_host_sanitized(verbose: bool = False) -> Path:
 
 if __name__ == "__main__":
     build(verbose=True)
+    build_bench(verbose=True)

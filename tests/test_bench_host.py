@@ -72,3 +72,13 @@ def test_summary_refuses_other_sources_and_unknown_kernels(tmp_path):
     _write_csv(dirs[0], "FETCH_SIZE", gone, 10.0)
     with pytest.raises(SystemExit, match="not in the current library"):
         bench.summarize_pmc("tiny", *dirs)
+
+
+def test_stream_read_helper_is_built_and_exported():
+    import shutil
+    lib = Path(bench.BENCH_LIB)
+    assert lib.exists(), "build() makes libpkv_bench.so"
+    nm = shutil.which("nm")
+    if nm:
+        out = subprocess.run([nm, "-D", str(lib)], capture_output=True, text=True).stdout
+        assert " T pkvb_stream_read" in out
