@@ -48,31 +48,64 @@ constexpr float kLazyRescale = 8.f;
 // of a wave's rows.)
 constexpr float kMaxFloor = -1e30f;
 
-// LDS layout.  The K tile's 16-byte slot of row r is XORed with 2*bit5(r),
-// and lane group g of a QK^T operand supplies the head dimensions of slot
-// KS*g + kk at step kk (any slot-to-k assignment is valid as long as the K
-// and Q operands agree); with a 17-slot row stride the operand reads are
-// free of bank conflicts, and the tile stores, one whole row per D/8 lanes,
-// are too.  V^T rows take a 10-slot stride, which makes the PV operand reads
-// conflict-free; its stores write one contiguous run of keys per dim row.
-// (Access patterns timed on this chip against contiguous accesses of the
-// same width.)
-__device__ __forceinline__ int ksw(int r) { return (r >> 4) & 2; }
+// LDS layout.  K and V tiles arrive by direct-to-LDS loads: one load
+// instruction writes its 64 lanes' 16-byte chunks to 1 KB of consecutive LDS
+// (lane l at byte 16 l), and each lane fetches the global chunk that belongs
+// at its position.  Tiles are row-major without padding; the 16-byte slot s
+// of tile row r sits at chunk r * SL + (s ^ swizzle(r)), SL = D / 8 slots per
+// row.  Timed on this chip, a wave's 16-byte LDS reads run at full rate when
+// every 8 consecutive lanes touch chunks that differ modulo 16 (256 bytes)
+// and every 32 consecutive lanes chunks that differ modulo 32 (512 bytes):
+// kswz() gives both for the QK^T operand reads of K rows (16 rows by two
+// slots per half-wave), vswz() the best rate measured for the transposing
+// reads (ds_read_b64_tr_b16) that give the PV operand from V rows.
+template <int SL>
+__device__ __forceinline__ int kswz(int r) {
+  if constexpr (SL == 16)
+    return ((r & 1) ^ ((r >> 4) & 1)) | (((r >> 1) & 1) << 1) | (((r >> 3) & 1) << 3);
+  else
+    return (((r >> 1) & 1) ^ ((r >> 4) & 1)) | (((r >> 3) & 1) << 2);
+}
+template <int SL>
+__device__ __forceinline__ int vswz(int r) {
+  if constexpr (SL == 16)
+    return 2 * ((r & 3) | (((r >> 3) & 1) << 2));
+  else
+    return 2 * (((r >> 1) & 1) | (((r >> 3) & 1) << 1));
+}
+
+#define PKV_AS1 __attribute__((address_space(1)))
+#define PKV_AS3 __attribute__((address_space(3)))
+
+// 16 bytes from global memory straight into LDS; `lds` must be the same in
+// every lane of the wave (it becomes the instruction's LDS base), and lane l
+// writes bytes 16 l .. 16 l + 15 above it.
+__device__ __forceinline__ void load_lds16(const void *g, void *lds) {
+  __builtin_amdgcn_global_load_lds((const PKV_AS1 void *)g, (PKV_AS3 void *)lds, 16, 0, 0);
+}
+
+typedef short s4_t __attribute__((ext_vector_type(4)));
+// Transposing LDS read: within each 16-lane group, lane j receives element
+// j % 4 of the four 8-byte chunks addressed by lanes j / 4 + 4 k, k = 0..3.
+__device__ __forceinline__ h4_t ld_tr16(const _Float16 *lds) {
+  const s4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PKV_AS3 s4_t *)(lds));
+  return __builtin_bit_cast(h4_t, v);
+}
 
 template <int D, int BS>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p,
                                                          int num_qtiles) {
   constexpr int BM = 128, BN = 64, WROWS = 32;
-  constexpr int KS = D / 32;    // MFMA steps over the head dimension (QK)
-  constexpr int DT = D / 16;    // 16-row blocks of O^T (PV)
-  constexpr int KPT = D / 32;   // keys per thread in a tile load
-  constexpr int NKG = BN / KPT; // key groups of a tile load
-  constexpr int KSTR = D + 8;   // K tile row stride in fp16 (16-byte pad)
-  constexpr int VSTR = BN + 16; // V^T tile row stride in fp16 (10 slots)
-  static_assert(NKG * (D / 8) == 256, "one 16-byte chunk per thread and key");
-  static_assert(BS % KPT == 0, "a thread's keys share a block");
-  __shared__ __attribute__((aligned(16))) _Float16 sK[2][BN * KSTR];
-  __shared__ __attribute__((aligned(16))) _Float16 sV[2][D * VSTR];
+  constexpr int KS = D / 32;   // MFMA steps over the head dimension (QK)
+  constexpr int DT = D / 16;   // 16-row blocks of O^T (PV)
+  constexpr int SL = D / 8;    // 16-byte slots of a row
+  constexpr int RPI = 64 / SL; // tile rows one load instruction fills
+  constexpr int NI = 16 / RPI; // load instructions per wave, tile and operand
+  // ids of distinct blocks among one wave's 16 tile rows
+  constexpr int NBW = BS >= 16 ? 1 : 16 / BS;
+  static_assert(BS % RPI == 0, "a load instruction's rows share a block");
+  __shared__ __attribute__((aligned(16))) _Float16 sK[2][BN * D];
+  __shared__ __attribute__((aligned(16))) _Float16 sV[2][BN * D];
   __shared__ int sBad;
 
   const int tid = threadIdx.x;
@@ -116,81 +149,62 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p,
   const int t_lo = sp * ntiles / nparts, t_hi = (sp + 1) * ntiles / nparts;
   const int32_t *trow = p.block_tables + (size_t)c * p.max_blocks_per_seq;
 
-  // Tile loader: the thread owns KPT consecutive keys of the K tile and
-  // KPT consecutive keys of the V tile, 8 dims (one 16-byte chunk) of each.
-  // K: chunk kcc = tid % (D/8) of keys KPT*kkg .. (kkg = tid / (D/8)), so
-  //    the D/8 lanes of a key row hold the whole row: every load instruction
-  //    reads whole rows and every LDS store writes whole rows (all banks,
-  //    no conflicts).
-  // V: chunk vcc = tid / NKG of keys KPT*vkg .. (vkg = tid % NKG), so the
-  //    lanes with one chunk hold consecutive keys, which the transposed V^T
-  //    store writes as one contiguous run per dim row (no conflicts).
-  // It has no branches (a load under a branch makes the compiler wait for
-  // it inside the branch, serialising the tile's loads):
-  // * the block ids of a later tile are read one tile ahead from clamped
-  //   (always valid) table indices and only checked where they are used; a
-  //   check right after its load would wait for every load issued before it
-  //   (memory counters retire in order);
-  // * K/V loads are unconditional (an absent key reads block 0, in bounds),
-  //   absent keys are zeroed when the tile is stored;
-  // * a block id outside the pool sets a per-thread flag, gathered once at
-  //   the end.
-  constexpr int LPR = D / 8;  // 16-byte chunks of a row
-  const int kcc = tid % LPR, kkg = tid / LPR;
-  const int vkg = tid % NKG, vcc = tid / NKG;
-  auto lookup = [&](int t, int kg) -> int {
-    const int pos = t * BN + KPT * kg;
-    return trow[min(pos, L - 1) / BS];  // L >= 1, L <= max_blocks_per_seq * BS
-  };
-  uint4 kreg[KPT], vreg[KPT];
-  unsigned klive = 0, vlive = 0;  // bit i: key i of this thread's slice exists
-  bool bad = false;               // a block id outside the pool was met
-  // The thread's KPT keys are consecutive and share one block (BS is a
-  // multiple of KPT); the block id is only meaningful when the first of them
-  // lies below L.  Returns the element offset of the first key's chunk.
-  auto locate = [&](int t, int kg, int cc, int ph, unsigned &live) -> size_t {
-    const int pos = t * BN + KPT * kg;
-    const bool want = t < t_hi && pos < L;
-    const bool oob = want && (ph < 0 || ph >= p.num_blocks);
-    bad |= oob;
-    const bool blk = want && !oob;
-    live = blk ? (1u << min(L - pos, KPT)) - 1u : 0u;
-    return blk ? (((size_t)ph * p.num_kv_heads + kvh) * BS + pos % BS) * D + 8 * cc
-               : (size_t)8 * cc;
-  };
-  auto load = [&](int t, int phk, int phv) {
-    const size_t koff = locate(t, kkg, kcc, phk, klive);
-    const size_t voff = locate(t, vkg, vcc, phv, vlive);
+  // Tile loader.  Wave w fills tile rows 16 w .. 16 w + 15 of K and of V
+  // with NI load instructions each; lane l of instruction j fills LDS chunk
+  // (NI w + j) * 64 + l, i.e. row 16 w + RPI j + l / SL, LDS slot l % SL,
+  // which holds the row's global slot (l % SL) ^ swizzle(row).  The rows of
+  // one instruction lie in one block (tile starts are multiples of BS or of
+  // 64), so its block id is the same in every lane: read with a scalar load
+  // one tile ahead, from a table index clamped to the last live key (always
+  // a valid entry), and only its base address differs between tiles.  An id
+  // outside the pool reads block 0 instead and sets a flag, gathered once at
+  // the end.  V rows of keys at or past the sequence length (tail slots of
+  // the last block, or a clamped block) are zeroed once they have landed:
+  // their weights are 0, and 0 times a non-finite value would not be.
+  int koff[NI], voff[NI];  // byte offsets of the lane's chunks in a block
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      kreg[i] = ld16(p.k_cache + koff + i * D);
-      vreg[i] = ld16(p.v_cache + voff + i * D);
+  for (int j = 0; j < NI; ++j) {
+    const int r = 16 * wave + RPI * j + lane / SL;
+    const int sl = lane % SL;
+    const int kr = r % BS;  // row within its block
+    koff[j] = (kr * D + 8 * (sl ^ kswz<SL>(r))) * 2;
+    voff[j] = (kr * D + 8 * (sl ^ vswz<SL>(r))) * 2;
+  }
+  const size_t head_elems = (size_t)BS * D;
+  auto tile_ids = [&](int t, int *ids) {
+#pragma unroll
+    for (int u = 0; u < NBW; ++u) {
+      const int key = uniform(min(t * BN + 16 * wave + BS * u, L - 1));
+      ids[u] = trow[key / BS];
     }
   };
-  auto store = [&](int buf) {
-    const uint4 zero = make_uint4(0, 0, 0, 0);
+  bool bad = false;  // a block id outside the pool was met
+  auto issue_tile = [&](int buf, const int *ids) {
+    size_t base[NBW];
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      if (!((klive >> i) & 1)) kreg[i] = zero;
-      if (!((vlive >> i) & 1)) vreg[i] = zero;
-      const int row = KPT * kkg + i;
-      st16(&sK[buf][row * KSTR + 8 * (kcc ^ ksw(row))], kreg[i]);
+    for (int u = 0; u < NBW; ++u) {
+      const int ph = uniform(ids[u]);
+      const bool oob = ph < 0 || ph >= p.num_blocks;
+      bad |= oob;
+      base[u] = ((size_t)(oob ? 0 : ph) * p.num_kv_heads + kvh) * head_elems;
     }
-    // V^T: dim 8*vcc + j, keys KPT*vkg .. +KPT-1 (KPT*2 contiguous bytes)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      _Float16 *dst = &sV[buf][(8 * vcc + j) * VSTR + KPT * vkg];
-      if constexpr (KPT == 4) {
-        h4_t t;
+    for (int j = 0; j < NI; ++j) {
+      const int u = (RPI * j) / BS;
+      load_lds16(reinterpret_cast<const char *>(p.k_cache + base[u]) + koff[j],
+                 &sK[buf][(NI * wave + j) * 512]);
+      load_lds16(reinterpret_cast<const char *>(p.v_cache + base[u]) + voff[j],
+                 &sV[buf][(NI * wave + j) * 512]);
+    }
+  };
+  // after this wave's loads of tile t have landed
+  auto zero_tail = [&](int t, int buf) {
+    if (t * BN + 16 * wave + 15 >= L) {
+      const uint4 zero = make_uint4(0, 0, 0, 0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) t[i] = as_h8(vreg[i])[j];
-        *reinterpret_cast<h4_t *>(dst) = t;
-      } else {
-        h2_t t;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) t[i] = as_h8(vreg[i])[j];
-        *reinterpret_cast<h2_t *>(dst) = t;
-      }
+      for (int j = 0; j < NI; ++j)
+        if (t * BN + 16 * wave + RPI * j + lane / SL >= L)
+          st16(&sV[buf][((NI * wave + j) * 64 + lane) * 8], zero);
     }
   };
 
@@ -209,11 +223,11 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p,
   for (int j = 0; j < 8; ++j) ones[j] = (_Float16)1.f;
 
   if (tid == 0) sBad = 0;
-  // Prologue, ordered so that only two memory latencies are exposed: the
-  // block ids of tiles 0 and 1, then the query rows (issued while the ids
-  // are in flight), then tile 0's K/V, which needs its id.
-  int phk_next = lookup(t_lo, kkg), phv_next = lookup(t_lo, vkg);
-  const int phk_one = lookup(t_lo + 1, kkg), phv_one = lookup(t_lo + 1, vkg);
+  // Prologue: the block ids of tiles t_lo and t_lo + 1, then the query rows
+  // (issued while the ids are in flight), then tile t_lo's loads.
+  int ids[NBW], ids_next[NBW];
+  tile_ids(t_lo, ids);
+  tile_ids(t_lo + 1, ids_next);
   // The wave's query rows as B operands: column lc of block qb, dims of
   // slot KS*g + kk (8 per slot).  Rows past the chunk load its last row
   // (unconditional loads, nothing waits inside a branch); their results are
@@ -226,21 +240,34 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p,
     for (int kk = 0; kk < KS; ++kk)
       qf[kk][qb] = as_h8(ld16(p.q + ((size_t)(q_begin + qr) * Hq + h) * D + 8 * (KS * g + kk)));
   }
-  load(t_lo, phk_next, phv_next);
-  phk_next = phk_one;
-  phv_next = phv_one;
-  store(0);
+  issue_tile(0, ids);
+  __builtin_amdgcn_s_waitcnt(0);
+  zero_tail(t_lo, 0);
   __syncthreads();
+
+  // Per-lane parts of the LDS operand addresses (in fp16 elements).
+  // K: A row lc of block mm is key 32*(mm/2) + 8*(lc/4) + 4*(mm%2) + lc%4;
+  // its swizzle depends on lc only.
+  const int kx = kswz<SL>(8 * (lc >> 2) + (lc & 3));
+  const int krow_lane = 8 * (lc >> 2) + (lc & 3);
+  // V (transposing reads): lane lc of group g addresses key row
+  // 32 ks + 8 g + 4 hh + lc / 4, dims 16 dt + 4 (lc % 4); the row's swizzle
+  // depends on lc and g only.
+  const int vrow_lane = 8 * g + (lc >> 2);
+  const int vx = vswz<SL>(vrow_lane);
 
   // The wave computes nothing when all its rows lie past the chunk.
   const bool wave_live = wq0 < qlen;
   for (int kt = t_lo; kt < t_hi; ++kt) {
     const int buf = (kt - t_lo) & 1;
     const int kbase = kt * BN;
-    // the next tile's loads (harmless past the last tile)
-    load(kt + 1, phk_next, phv_next);
-    phk_next = lookup(kt + 2, kkg);
-    phv_next = lookup(kt + 2, vkg);
+    // the next tile's loads into the other buffer (its last readers passed
+    // the barrier that ended the previous iteration), then the ids of the
+    // tile after it
+    if (kt + 1 < t_hi) {
+      issue_tile(buf ^ 1, ids_next);
+      tile_ids(kt + 2, ids_next);
+    }
     // skip a tile that lies wholly above this wave's diagonal
     if (wave_live && kbase <= P + wq0 + WROWS - 1) {
       const _Float16 *Kt = sK[buf];
@@ -251,18 +278,14 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p,
       // fragments are read one step ahead.
       f4_t st[4][2];
       h8_t fa[2][4];
-      int krow[4], ksl[4];
 #pragma unroll
-      for (int mm = 0; mm < 4; ++mm) {
-        // A row lc of block mm is key 32*(mm/2) + 8*(lc/4) + 4*(mm%2) + lc%4
-        krow[mm] = 32 * (mm >> 1) + 8 * (lc >> 2) + 4 * (mm & 1) + (lc & 3);
-        ksl[mm] = ksw(krow[mm]);
-        st[mm][0] = st[mm][1] = f4_t{0.f, 0.f, 0.f, 0.f};
-      }
+      for (int mm = 0; mm < 4; ++mm) st[mm][0] = st[mm][1] = f4_t{0.f, 0.f, 0.f, 0.f};
       auto read_k = [&](int kk, h8_t *dst) {
 #pragma unroll
-        for (int mm = 0; mm < 4; ++mm)
-          dst[mm] = as_h8(ld16(&Kt[krow[mm] * KSTR + 8 * ((KS * g + kk) ^ ksl[mm])]));
+        for (int mm = 0; mm < 4; ++mm) {
+          const int r = 32 * (mm >> 1) + 4 * (mm & 1) + krow_lane;
+          dst[mm] = as_h8(ld16(&Kt[(r * SL + ((KS * g + kk) ^ kx)) * 8]));
+        }
       };
       read_k(0, fa[0]);
 #pragma unroll
@@ -331,10 +354,17 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p,
       }
       // O^T[d][q] += sum_k V^T[d][k] P^T[k][q]; slot j of lane group g is key
       // 32ks + 8g + j on both sides.  Step i = (ks, dt); its V^T fragment
-      // is read NFB steps ahead.
+      // (two transposing reads, keys +0..3 and +4..7) is read NFB steps
+      // ahead.
       constexpr int NFB = 2;
       auto read_v = [&](int i) {
-        return as_h8(ld16(&Vt[(16 * (i % DT) + lc) * VSTR + 32 * (i / DT) + 8 * g]));
+        const int ks = i / DT, dt = i % DT;
+        const int r0 = 32 * ks + vrow_lane;  // + 4 for the second half
+        const int slot = (2 * dt + ((lc >> 1) & 1)) ^ vx;
+        const int e0 = (r0 * SL + slot) * 8 + 4 * (lc & 1);
+        const h4_t lo = ld_tr16(&Vt[e0]);
+        const h4_t hi = ld_tr16(&Vt[e0 + 4 * SL * 8]);
+        return h8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       };
       h8_t fb[NFB];
 #pragma unroll
@@ -352,7 +382,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p,
         lacc[1] = mfma16x16x32(ones, pb[ks][1], lacc[1]);
       }
     }
-    if (kt + 1 < t_hi) store(buf ^ 1);
+    // the next tile has landed (this wave's part), its dead V rows are
+    // cleared, then every wave's part is visible after the barrier
+    __builtin_amdgcn_s_waitcnt(0);
+    if (kt + 1 < t_hi) zero_tail(kt + 1, buf ^ 1);
     __syncthreads();
   }
 
