@@ -84,6 +84,12 @@ __device__ __forceinline__ void load_lds16(const void *g, void *lds) {
   __builtin_amdgcn_global_load_lds((const PKV_AS1 void *)g, (PKV_AS3 void *)lds, 16, 0, 0);
 }
 
+// A tile buffer index known at compile time.
+template <int B>
+struct Buf {
+  static constexpr int value = B;
+};
+
 typedef short s4_t __attribute__((ext_vector_type(4)));
 // Transposing LDS read: within each 16-lane group, lane j receives element
 // j % 4 of the four 8-byte chunks addressed by lanes j / 4 + 4 k, k = 0..3.
@@ -104,8 +110,18 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p,
   // ids of distinct blocks among one wave's 16 tile rows
   constexpr int NBW = BS >= 16 ? 1 : 16 / BS;
   static_assert(BS % RPI == 0, "a load instruction's rows share a block");
-  __shared__ __attribute__((aligned(16))) _Float16 sK[2][BN * D];
-  __shared__ __attribute__((aligned(16))) _Float16 sV[2][BN * D];
+  // Two buffers of each tile, as separate variables: every access names its
+  // buffer at compile time (the key-tile loop is unrolled by two), so the
+  // compiler can tell the reads of one buffer from the direct-to-LDS loads
+  // in flight into the other and need not wait for those loads first.
+  __shared__ __attribute__((aligned(16))) _Float16 sK0[BN * D], sK1[BN * D];
+  __shared__ __attribute__((aligned(16))) _Float16 sV0[BN * D], sV1[BN * D];
+  auto kbuf = [&](auto b) -> _Float16 * {
+    if constexpr (decltype(b)::value == 0) return sK0; else return sK1;
+  };
+  auto vbuf = [&](auto b) -> _Float16 * {
+    if constexpr (decltype(b)::value == 0) return sV0; else return sV1;
+  };
   __shared__ int sBad;
 
   const int tid = threadIdx.x;
@@ -179,7 +195,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p,
     }
   };
   bool bad = false;  // a block id outside the pool was met
-  auto issue_tile = [&](int buf, const int *ids) {
+  auto issue_tile = [&](auto buf, const int *ids) {
     size_t base[NBW];
 #pragma unroll
     for (int u = 0; u < NBW; ++u) {
@@ -192,19 +208,19 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p,
     for (int j = 0; j < NI; ++j) {
       const int u = (RPI * j) / BS;
       load_lds16(reinterpret_cast<const char *>(p.k_cache + base[u]) + koff[j],
-                 &sK[buf][(NI * wave + j) * 512]);
+                 kbuf(buf) + (NI * wave + j) * 512);
       load_lds16(reinterpret_cast<const char *>(p.v_cache + base[u]) + voff[j],
-                 &sV[buf][(NI * wave + j) * 512]);
+                 vbuf(buf) + (NI * wave + j) * 512);
     }
   };
   // after this wave's loads of tile t have landed
-  auto zero_tail = [&](int t, int buf) {
+  auto zero_tail = [&](int t, auto buf) {
     if (t * BN + 16 * wave + 15 >= L) {
       const uint4 zero = make_uint4(0, 0, 0, 0);
 #pragma unroll
       for (int j = 0; j < NI; ++j)
         if (t * BN + 16 * wave + RPI * j + lane / SL >= L)
-          st16(&sV[buf][((NI * wave + j) * 64 + lane) * 8], zero);
+          st16(vbuf(buf) + ((NI * wave + j) * 64 + lane) * 8, zero);
     }
   };
 
@@ -240,9 +256,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p,
     for (int kk = 0; kk < KS; ++kk)
       qf[kk][qb] = as_h8(ld16(p.q + ((size_t)(q_begin + qr) * Hq + h) * D + 8 * (KS * g + kk)));
   }
-  issue_tile(0, ids);
+  issue_tile(Buf<0>{}, ids);
   __builtin_amdgcn_s_waitcnt(0);
-  zero_tail(t_lo, 0);
+  zero_tail(t_lo, Buf<0>{});
   __syncthreads();
 
   // Per-lane parts of the LDS operand addresses (in fp16 elements).
@@ -258,20 +274,21 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p,
 
   // The wave computes nothing when all its rows lie past the chunk.
   const bool wave_live = wq0 < qlen;
-  for (int kt = t_lo; kt < t_hi; ++kt) {
-    const int buf = (kt - t_lo) & 1;
+  // One key tile; buffer `buf` holds it, the other receives the next tile.
+  auto step = [&](auto buf, int kt) {
+    constexpr Buf<1 - decltype(buf)::value> next{};
     const int kbase = kt * BN;
     // the next tile's loads into the other buffer (its last readers passed
-    // the barrier that ended the previous iteration), then the ids of the
-    // tile after it
+    // the barrier that ended the previous step), then the ids of the tile
+    // after it
     if (kt + 1 < t_hi) {
-      issue_tile(buf ^ 1, ids_next);
+      issue_tile(next, ids_next);
       tile_ids(kt + 2, ids_next);
     }
     // skip a tile that lies wholly above this wave's diagonal
     if (wave_live && kbase <= P + wq0 + WROWS - 1) {
-      const _Float16 *Kt = sK[buf];
-      const _Float16 *Vt = sV[buf];
+      const _Float16 *Kt = kbuf(buf);
+      const _Float16 *Vt = vbuf(buf);
       // S^T: the head-dimension step is the outer loop, so the eight
       // accumulators (4 key blocks x 2 query blocks) are independent and
       // back-to-back MFMAs never wait on each other; each step's four K
@@ -385,8 +402,12 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p,
     // the next tile has landed (this wave's part), its dead V rows are
     // cleared, then every wave's part is visible after the barrier
     __builtin_amdgcn_s_waitcnt(0);
-    if (kt + 1 < t_hi) zero_tail(kt + 1, buf ^ 1);
+    if (kt + 1 < t_hi) zero_tail(kt + 1, next);
     __syncthreads();
+  };
+  for (int kt = t_lo; kt < t_hi; kt += 2) {
+    step(Buf<0>{}, kt);
+    if (kt + 1 < t_hi) step(Buf<1>{}, kt + 1);
   }
 
   if (bad) sBad = 1;
