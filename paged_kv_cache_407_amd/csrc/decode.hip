@@ -396,54 +396,80 @@ __global__ __launch_bounds__(256) void decode_gqa_mfma_kernel(DecodeParams p) {
   using KRegs = uint4[2][KNI];           // K: tile i, row q*KRPI + krow, chunk kcol
   using VRegs = uint32_t[2][4][VD / 2];  // V: tile i, token 16i + 4g + r of the step
   // VD fp16 of one V row (16 or 8 bytes), or zeros
-  auto load_v = [&](uint32_t (&dst)[VD / 2], bool in, const _Float16 *src) {
+  // Loads are unconditional and keep what they read: a row outside the
+  // partition reads a block of the pool (every settled id is one), and every
+  // row past the last valid token -- those included -- has its score
+  // replaced by -inf and its V row by zeros in compute_step.  A load under a
+  // branch, or a select right after it, would make the compiler wait for
+  // that load before issuing the next ones.
+  auto load_v = [&](uint32_t (&dst)[VD / 2], const _Float16 *src) {
     if constexpr (VD == 8) {
-      const uint4 v = in ? ld16_nt(src) : zero;
+      const uint4 v = ld16_nt(src);
       dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
     } else {
-      const uint2 v = in ? ld8_nt(src) : make_uint2(0, 0);
+      const uint2 v = ld8_nt(src);
       dst[0] = v.x; dst[1] = v.y;
     }
   };
+  // All K loads of the step are issued before its V loads: the K tile is
+  // stored and consumed (scores, softmax) while the V loads are still in
+  // flight, and the wait before the K store counts only the K loads.
   auto load_step = [&](int b, KRegs &kr, VRegs &vr) {
+    if constexpr (!TWO) {
+      bool in[2];
+      const _Float16 *kb[2], *vb[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      if constexpr (!TWO) {
+      for (int i = 0; i < 2; ++i) {
         // tile i lies in block b + 16i/BS, from its row 16i % BS
         const int bi = (16 * i) / BS;
-        const bool in = b + bi < blk1;
-        const int phys = block_id(in ? b + bi - blk0 : 0);
+        in[i] = b + bi < blk1;
+        const int phys = block_id(in[i] ? b + bi - blk0 : 0);
         const size_t base = ((size_t)phys * p.num_kv_heads + kvh) * head_elems +
                             (size_t)((16 * i) % BS) * D;
-        const _Float16 *kb = p.k_cache + base + (size_t)krow * D + 8 * kcol;
-        const _Float16 *vb = p.v_cache + base + (size_t)(4 * g) * D + VD * hc;
+        kb[i] = p.k_cache + base + (size_t)krow * D + 8 * kcol;
+        vb[i] = p.v_cache + base + (size_t)(4 * g) * D + VD * hc;
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int q = 0; q < KNI; ++q)
-          kr[i][q] = in ? ld16_nt(kb + (size_t)q * KRPI * D) : zero;
+        kr[i][q] = ld16_nt(kb[i] + (size_t)q * KRPI * D);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) load_v(vr[i][r], in, vb + (size_t)r * D);
-      } else {
-        // block size 8: rows 0-7 of tile i in block A = b + 2i, rows 8-15 in
-        // block B = b + 2i + 1.  K load q holds rows q*KRPI .. +KRPI-1 (one
-        // block); V row 4g + r is in block B for g >= 2.
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) load_v(vr[i][r], vb[i] + (size_t)r * D);
+    } else {
+      // block size 8: rows 0-7 of tile i in block A = b + 2i, rows 8-15 in
+      // block B = b + 2i + 1.  K load q holds rows q*KRPI .. +KRPI-1 (one
+      // block); V row 4g + r is in block B for g >= 2.
+      bool inA[2], inB[2];
+      size_t baseA[2], baseB[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
         const int bA = b + 2 * i, bB = bA + 1;
-        const bool inA = bA < blk1, inB = bB < blk1;
-        const int phA = block_id(inA ? bA - blk0 : 0);
-        const int phB = block_id(inB ? bB - blk0 : 0);
-        const size_t baseA = ((size_t)phA * p.num_kv_heads + kvh) * head_elems;
-        const size_t baseB = ((size_t)phB * p.num_kv_heads + kvh) * head_elems;
+        inA[i] = bA < blk1;
+        inB[i] = bB < blk1;
+        const int phA = block_id(inA[i] ? bA - blk0 : 0);
+        const int phB = block_id(inB[i] ? bB - blk0 : 0);
+        baseA[i] = ((size_t)phA * p.num_kv_heads + kvh) * head_elems;
+        baseB[i] = ((size_t)phB * p.num_kv_heads + kvh) * head_elems;
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int q = 0; q < KNI; ++q) {
           const bool hi = q * KRPI >= BS;
-          const size_t off = (hi ? baseB : baseA) +
+          const size_t off = (hi ? baseB[i] : baseA[i]) +
                              (size_t)((q * KRPI + krow) % BS) * D + 8 * kcol;
-          kr[i][q] = (hi ? inB : inA) ? ld16_nt(p.k_cache + off) : zero;
+          kr[i][q] = ld16_nt(p.k_cache + off);
         }
-        const bool vhi = g >= 2;
-        const _Float16 *vb = p.v_cache + (vhi ? baseB : baseA) + VD * hc;
+      const bool vhi = g >= 2;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const _Float16 *vb = p.v_cache + (vhi ? baseB[i] : baseA[i]) + VD * hc;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          load_v(vr[i][r], vhi ? inB : inA, vb + (size_t)((4 * g + r) % BS) * D);
+          load_v(vr[i][r], vb + (size_t)((4 * g + r) % BS) * D);
       }
     }
   };
