@@ -11,10 +11,10 @@
 // * One workgroup of 4 waves takes a 128-row query tile of one (chunk, head);
 //   each wave owns 32 query rows (two 16-column MFMA blocks), so every
 //   operand fragment read from LDS feeds two MFMAs.
-// * Key/value tiles of 64 tokens are gathered from the paged pool (one
-//   block-table lookup per thread and tile) into double-buffered LDS: the
-//   next tile's global loads are in flight while the current one is
-//   consumed.  K is stored row-major; V is stored transposed ([dim][key]).
+// * Key/value tiles of 64 tokens go from the paged pool straight into LDS
+//   (direct-to-LDS loads, one block id per load instruction, read one tile
+//   ahead); two buffers per operand, so the next tile's loads are in flight
+//   while the current one is consumed.  K and V stay row-major.
 // * Per tile and wave:
 //     S^T = K Q^T     A = 16 keys x 32 dims from LDS, B = the wave's query
 //                     rows, kept in registers;
@@ -25,13 +25,18 @@
 //                     weights, at most 256, stay exact enough in fp16), so
 //                     the O rescale is rare;
 //     O^T += V^T P^T  the accumulator layout of S^T is the B-operand layout
-//                     of P^T, so the fp16 weights never leave their lanes.
+//                     of P^T, so the fp16 weights never leave their lanes;
+//                     the V^T operand comes from V rows by two transposing
+//                     LDS reads (ds_read_b64_tr_b16) per 8 keys.
 //   The 16 keys of each S^T block are taken in a permuted order chosen so
 //   that lane group g ends up holding 8 consecutive keys of each 32-key
-//   step; the V^T operand of PV is then one 16-byte LDS read.
+//   step, the keys the V^T operand's transposing reads deliver.
 // * Keys above the diagonal are removed by selection in the diagonal tiles
 //   only; a wave skips tiles that lie wholly above its rows.  The heaviest
 //   query tiles (last in their chunk) are dispatched first.
+// * When the query tiles are too few to fill the chip, each one's key range
+//   is cut into parts run by different workgroups, merged by a second
+//   kernel.
 #include "common.hpp"
 #include "kernels.hpp"
 
