@@ -29,9 +29,10 @@
 //   four VGPRs hold the partition's block ids: lane j keeps entries j,
 //   64 + j, ... and a wave reads them with v_readlane; for blocks smaller
 //   than one wave-wide load, at most 64 blocks, and each lane fetches its
-//   token's entry with a lane permute).  One workgroup of 8 waves (fewer when a partition holds fewer
-//   wave steps) takes one (partition, sequence, head group); waves take
-//   interleaved steps of whole blocks and are merged through LDS.
+//   token's entry with a lane permute).  One workgroup of 8 waves (fewer
+//   when a partition holds fewer wave steps) takes one (partition,
+//   sequence, head group); waves take interleaved steps of whole blocks and
+//   are merged through LDS.
 // * With several partitions, each workgroup stores (max, sum, unnormalised
 //   output) and decode_merge_kernel combines them: M = max_i m_i,
 //   out = sum_i 2^(m_i-M) o_i / sum_i 2^(m_i-M) l_i -- the rescaling of the
