@@ -24,7 +24,10 @@ Roofline of the dominant call (decode): algorithmic bytes per launch (KV rows
 read once -- each physical (block, offset) once -- plus queries and outputs)
 divided by its launch duration, against the 8 TB/s datasheet peak and, as
 frac_of_stream_read, against a plain sequential read of 4 GiB timed the same
-way on the same device (``stream_read``).  Durations come from HIP events on the
+way on the same device (``stream_read``).  The mixed step's prefill FLOP rate
+is likewise set against the 2.5 PFLOP/s datasheet figure and, as
+frac_of_mfma_reference, against an MFMA-only kernel of the same instruction
+(``mfma_reference``).  Durations come from HIP events on the
 launch stream around batches of back-to-back calls (a spin kernel keeps the
 GPU ahead of the host), divided by the batch size; the median over batches
 is reported with its p10 / p90.  This does not depend on --steps.
@@ -332,6 +335,52 @@ def launch_stats(call, batches=TIMING_BATCHES, per_batch=TIMING_CALLS) -> dict:
 STREAM_BYTES = 4 << 30
 STREAM_GRIDS = (8192, 32768, 65536, 131072)
 BENCH_LIB = os.path.join(ROOT, "paged_kv_cache_407_amd", "libpkv_bench.so")
+
+
+MFMA_ITERS = 1024
+MFMA_GRIDS = (256, 512, 1024, 2048)
+MFMA_SHAPES = {"f16_16x16x32": (0, 16 * 16 * 32 * 2, 8), "f16_32x32x16": (1, 32 * 32 * 16 * 2, 4)}
+
+
+def mfma_reference(dev) -> dict:
+    """What the matrix cores sustain on this device: MFMA-only kernels of
+    libpkv_bench.so (each wave issues independent accumulator chains of one
+    fp16 shape and nothing else), timed like the prefill (launch_stats), best
+    of a few grid sizes, per shape.  The prefill uses the 16x16x32 shape; its
+    FLOP rate is also reported as a fraction of that shape's reference."""
+    import ctypes
+    import torch
+    if not os.path.exists(BENCH_LIB):
+        raise SystemExit(f"{BENCH_LIB} is missing: run __graft_entry__.build() first")
+    lib = ctypes.CDLL(BENCH_LIB)
+    fn = lib.pkvb_mfma_rate
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                   ctypes.c_float, ctypes.c_float, ctypes.c_void_p]
+    out = torch.empty(max(MFMA_GRIDS) * 256, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    res = {}
+    for name, (shape, flop_per_inst, chains) in MFMA_SHAPES.items():
+        best = None
+        for grid in MFMA_GRIDS:
+            def call(_i, grid=grid, shape=shape):
+                rc = fn(out.data_ptr(), shape, grid, MFMA_ITERS, 0.125, 0.125, stream)
+                if rc:
+                    raise RuntimeError(f"pkvb_mfma_rate failed: hip error {rc}")
+            call(0)
+            torch.cuda.synchronize()
+            st = launch_stats(call, batches=5, per_batch=5)
+            flops = grid * 4 * MFMA_ITERS * chains * flop_per_inst
+            tf = flops / (st["us_median"] * 1e-6) / 1e12
+            log(f"mfma {name}, {grid} workgroups: {st['us_median']} us, {tf:.1f} TFLOP/s")
+            if best is None or tf > best["TFLOPs"]:
+                best = {"TFLOPs": round(tf, 1), "frac_of_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
+                        "workgroups": grid, "us_median": st["us_median"],
+                        "kernel": f"mfma{name[4:]}_kernel (libpkv_bench.so)"}
+        res[name] = best
+    del out
+    torch.cuda.synchronize()
+    return res
 
 
 def stream_read_reference(dev) -> dict:
@@ -651,6 +700,12 @@ def main():
     for r in [line, *line.get("per_config", {}).values()]:
         if "roofline" in r:
             r["roofline"]["frac_of_stream_read"] = round(r["roofline"]["achieved"] / sr["GBps"], 4)
+    mr = mfma_reference(dev)
+    line["mfma_reference"] = mr
+    for r in [line, *line.get("per_config", {}).values()]:
+        if "prefill" in r:
+            r["prefill"]["frac_of_mfma_reference"] = round(
+                r["prefill"]["tflops"] / mr["f16_16x16x32"]["TFLOPs"], 4)
     print(json.dumps(line), flush=True)
 
 

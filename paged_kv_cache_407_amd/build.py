@@ -71,22 +71,25 @@ def build(verbose: bool = False, jobs: int | None = None) -> Path:
     return LIB
 
 
-# Measurement helper, apart from the library: a streaming-read kernel that
-# bench.py times as the reference for a plain sequential read of HBM.
-BENCH_SRC = CSRC / "bench" / "stream_read.hip"
+# Measurement helpers, apart from the library: a streaming-read kernel that
+# bench.py times as the reference for a plain sequential read of HBM, and
+# MFMA-only kernels, the reference for what the matrix cores sustain.
+BENCH_SRCS = [CSRC / "bench" / "stream_read.hip", CSRC / "bench" / "mfma_rate.hip"]
 BENCH_LIB = HERE / "libpkv_bench.so"
 
 
 def build_bench(verbose: bool = False) -> Path:
     tmp = BENCH_LIB.with_suffix(".so.tmp")
-    cmd = [hipcc(), *FLAGS, "-shared", "-o", str(tmp), str(BENCH_SRC)]
+    # accumulators of the MFMA-only kernels in VGPRs, as the prefill keeps them
+    cmd = [hipcc(), *FLAGS, "-mllvm", "--amdgpu-mfma-vgpr-form", "-shared", "-o", str(tmp),
+           *map(str, BENCH_SRCS)]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode:
         noise = "is not a recognized feature for this target"
         err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)
-        raise RuntimeError(f"hipcc failed on {BENCH_SRC.name}:\n{err}")
+        raise RuntimeError(f"hipcc failed on the measurement helpers:\n{err}")
     os.replace(tmp, BENCH_LIB)
     return BENCH_LIB
 

@@ -74,7 +74,7 @@ def test_summary_refuses_other_sources_and_unknown_kernels(tmp_path):
         bench.summarize_pmc("tiny", *dirs)
 
 
-def test_stream_read_helper_is_built_and_exported():
+def test_measurement_helpers_are_built_and_exported():
     import shutil
     lib = Path(bench.BENCH_LIB)
     assert lib.exists(), "build() makes libpkv_bench.so"
@@ -82,3 +82,4 @@ def test_stream_read_helper_is_built_and_exported():
     if nm:
         out = subprocess.run([nm, "-D", str(lib)], capture_output=True, text=True).stdout
         assert " T pkvb_stream_read" in out
+        assert " T pkvb_mfma_rate" in out
