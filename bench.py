@@ -24,7 +24,9 @@ Roofline of the dominant call (decode): algorithmic bytes per launch (KV rows
 read once -- each physical (block, offset) once -- plus queries and outputs)
 divided by its launch duration, against the 8 TB/s datasheet peak and, as
 frac_of_stream_read, against a plain sequential read of 4 GiB timed the same
-way on the same device (``stream_read``).  The mixed step's prefill FLOP rate
+way on the same device (``stream_read``), and as frac_of_stream_read_same_bytes
+against a read of the call's own byte count (cold windows of the same buffer),
+which pays the same launch, ramp and drain as a call that short.  The mixed step's prefill FLOP rate
 is likewise set against the 2.5 PFLOP/s datasheet figure and, as
 frac_of_mfma_reference, against an MFMA-only kernel of the same instruction
 (``mfma_reference``).  Durations come from HIP events on the
@@ -383,12 +385,16 @@ def mfma_reference(dev) -> dict:
     return res
 
 
-def stream_read_reference(dev) -> dict:
+def stream_read_reference(dev, sizes=()) -> tuple[dict, dict]:
     """What a plain sequential read of HBM reaches on this device: the
     streaming-read kernel of libpkv_bench.so (16-byte nontemporal loads, the
-    decode's load form; two streams, the halves of a 4 GiB buffer), timed like the decode
-    (launch_stats), best of a few grid sizes.  The decode's achieved
-    bandwidth is also reported as a fraction of it."""
+    decode's load form; two streams, the halves of the buffer), timed like
+    the decode (launch_stats), best of a few grid sizes.  First over a whole
+    4 GiB buffer; then, for each byte count in `sizes`, over windows of that
+    size taken in turn from the same buffer (each window last read 4 GiB
+    earlier, so cold like the decode's replicas): a short call pays the
+    same launch, ramp and drain as the decode call of that size.  Returns
+    (the 4 GiB figure, {bytes: figure})."""
     import ctypes
     import torch
     if not os.path.exists(BENCH_LIB):
@@ -401,25 +407,33 @@ def stream_read_reference(dev) -> dict:
     buf = torch.ones(STREAM_BYTES // 4, dtype=torch.int32, device=dev)
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream().cuda_stream
-    best = None
-    for grid in STREAM_GRIDS:
-        def call(_i, grid=grid):
-            rc = fn(buf.data_ptr(), STREAM_BYTES, sink.data_ptr(), grid, stream)
-            if rc:
-                raise RuntimeError(f"pkvb_stream_read failed: hip error {rc}")
-        call(0)
-        torch.cuda.synchronize()
-        st = launch_stats(call, batches=5, per_batch=5)
-        gbs = STREAM_BYTES / (st["us_median"] * 1e-6) / 1e9
-        log(f"stream read, {grid} workgroups: {st['us_median']} us, {gbs:.1f} GB/s")
-        if best is None or gbs > best["GBps"]:
-            best = {"GBps": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
-                    "bytes": STREAM_BYTES, "workgroups": grid, "us_median": st["us_median"],
-                    "kernel": "stream_read_kernel (libpkv_bench.so)"}
+
+    def best_of(nbytes):
+        windows = max(1, STREAM_BYTES // nbytes)
+        best = None
+        for grid in STREAM_GRIDS:
+            def call(i, grid=grid):
+                off = (i % windows) * nbytes
+                rc = fn(buf.data_ptr() + off, nbytes, sink.data_ptr(), grid, stream)
+                if rc:
+                    raise RuntimeError(f"pkvb_stream_read failed: hip error {rc}")
+            call(0)
+            torch.cuda.synchronize()
+            st = launch_stats(call, batches=5, per_batch=5)
+            gbs = nbytes / (st["us_median"] * 1e-6) / 1e9
+            log(f"stream read of {nbytes} B, {grid} workgroups: {st['us_median']} us, {gbs:.1f} GB/s")
+            if best is None or gbs > best["GBps"]:
+                best = {"GBps": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+                        "bytes": nbytes, "workgroups": grid, "us_median": st["us_median"],
+                        "kernel": "stream_read_kernel (libpkv_bench.so)"}
+        return best
+
+    whole = best_of(STREAM_BYTES)
+    per_size = {n: best_of(n) for n in sorted(set(sizes)) if 0 < n < STREAM_BYTES}
     del buf, sink
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
-    return best
+    return whole, per_size
 
 
 def to_device(a, dev):
@@ -695,11 +709,18 @@ def main():
         line["per_config"] = {}
         for name in extra:
             line["per_config"][name] = measure(name, args, dev, cpu and cpu / 3)
-    sr = stream_read_reference(dev)
+    recs = [line, *line.get("per_config", {}).values()]
+    same = [r["roofline"]["alg_bytes_per_launch"] // 16 * 16 for r in recs if "roofline" in r]
+    sr, sr_sized = stream_read_reference(dev, same)
     line["stream_read"] = sr
-    for r in [line, *line.get("per_config", {}).values()]:
+    for r in recs:
         if "roofline" in r:
-            r["roofline"]["frac_of_stream_read"] = round(r["roofline"]["achieved"] / sr["GBps"], 4)
+            rl = r["roofline"]
+            rl["frac_of_stream_read"] = round(rl["achieved"] / sr["GBps"], 4)
+            ref = sr_sized.get(rl["alg_bytes_per_launch"] // 16 * 16)
+            if ref:
+                rl["stream_read_same_bytes"] = ref
+                rl["frac_of_stream_read_same_bytes"] = round(rl["achieved"] / ref["GBps"], 4)
     mr = mfma_reference(dev)
     line["mfma_reference"] = mr
     for r in [line, *line.get("per_config", {}).values()]:
