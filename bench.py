@@ -32,7 +32,10 @@ frac_of_mfma_reference, against an MFMA-only kernel of the same instruction
 (``mfma_reference``).  Durations come from HIP events on the
 launch stream around batches of back-to-back calls (a spin kernel keeps the
 GPU ahead of the host), divided by the batch size; the median over batches
-is reported with its p10 / p90.  This does not depend on --steps.
+is reported with its p10 / p90.  This does not depend on --steps.  The step
+time itself is ms_per_step (K steps / K); its spread comes from batches of
+back-to-back steps through the same graphs (step_us_median, step_us_p10,
+step_us_p90).
 
 CPU baseline: the CPU oracle (test infrastructure) timed on the host cores on
 a bounded sample of the same batch's rows, median of 3 runs; the pool copy
@@ -583,6 +586,18 @@ def measure(name: str, args, dev, cpu_seconds: float | None) -> dict:
     ms_per_step = gpu_ms / K
     log(f"{name}: {K} steps: {gpu_ms:.3f} ms GPU, {wall_ms:.3f} ms wall")
 
+    # the spread of whole steps: batches of back-to-back steps through the same
+    # graphs (or eager steps), per-step time = batch time / steps per batch
+    if graphs is not None:
+        n_rounds = max(1, TIMING_CALLS // R)
+        sst = launch_stats(lambda i: rounds.replay(), per_batch=n_rounds)
+        steps_per_call = R
+    else:
+        sst = launch_stats(lambda i: step(reps[i % R]))
+        steps_per_call = 1
+    step_spread = {f"step_{k}": round(sst[k] / steps_per_call, 3)
+                   for k in ("us_median", "us_p10", "us_p90")}
+
     # launch durations, independent of K (GPU kept ahead of the host)
     def timed(fn):
         return launch_stats(lambda i: fn(reps[i % R]))
@@ -615,6 +630,7 @@ def measure(name: str, args, dev, cpu_seconds: float | None) -> dict:
         "kv_bytes_per_step": kv_bytes,
         "kv_bytes_logical": kvb["logical"],
         "wall_ms_per_step": round(wall_ms / K, 6),
+        **step_spread,
         "append_us_median": res["append"]["us_median"],
     }
     if S:
