@@ -83,10 +83,23 @@ __device__ __forceinline__ int vswz(int r) {
 #define PKV_AS3 __attribute__((address_space(3)))
 
 // 16 bytes from global memory straight into LDS; `lds` must be the same in
-// every lane of the wave (it becomes the instruction's LDS base), and lane l
-// writes bytes 16 l .. 16 l + 15 above it.
+// every lane of the wave (it becomes the instruction's LDS base, in M0), and
+// lane l writes bytes 16 l .. 16 l + 15 above it.
+//
+// Written as the instruction itself rather than the compiler builtin: while
+// the compiler tracks a direct-to-LDS load in flight, it treats the LDS
+// return counter as unordered and waits for every outstanding LDS read
+// (lgkmcnt(0)) before each use of one, so the operand reads of the current
+// tile lost all overlap with the MFMAs.  Untracked, its waits are partial
+// again.  The instruction writes no register, only LDS; every reader of the
+// buffer it fills runs after this kernel's explicit wait for all memory
+// counters and a barrier.
 __device__ __forceinline__ void load_lds16(const void *g, void *lds) {
-  __builtin_amdgcn_global_load_lds((const PKV_AS1 void *)g, (PKV_AS3 void *)lds, 16, 0, 0);
+  const unsigned base = (unsigned)(size_t)(PKV_AS3 void *)lds;
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(base)
+               : "memory", "m0");
 }
 
 // A tile buffer index known at compile time.
