@@ -322,15 +322,20 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p,
           dst[mm] = as_h8(ld16(&Kt[(r * SL + ((KS * g + kk) ^ kx)) * 8]));
         }
       };
+      // Scheduling barriers keep that order: under register pressure the
+      // scheduler would sink each read next to its MFMA, and every read's
+      // LDS latency would land on the tile's chain.
       read_k(0, fa[0]);
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
         if (kk + 1 < KS) read_k(kk + 1, fa[(kk + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int mm = 0; mm < 4; ++mm) {
           st[mm][0] = mfma16x16x32(fa[kk & 1][mm], qf[kk][0], st[mm][0]);
           st[mm][1] = mfma16x16x32(fa[kk & 1][mm], qf[kk][1], st[mm][1]);
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
 
       // lane holds keys kbase + 32*(mm/2) + 8g + 4*(mm%2) + r of column lc
@@ -408,6 +413,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p,
       for (int i = 0; i < 2 * DT; ++i) {
         const h8_t a = fb[i % NFB];
         if (i + NFB < 2 * DT) fb[i % NFB] = read_v(i + NFB);
+        __builtin_amdgcn_sched_barrier(0);  // the reads stay NFB steps ahead
         o[i % DT][0] = mfma16x16x32(a, pb[i / DT][0], o[i % DT][0]);
         o[i % DT][1] = mfma16x16x32(a, pb[i / DT][1], o[i % DT][1]);
       }
