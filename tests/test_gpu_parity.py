@@ -367,6 +367,38 @@ def test_prefill_small(spec):
     check_decode(b, kc, vc, dec)
 
 
+def _random_prefill_specs(n=12, seed=4242):
+    """Seeded random shapes over every compiled prefill instance: head dim
+    64 or 128, block size 8, 16 or 32, 1 to 4 query heads per KV head, 1 to
+    4 chunks whose lengths and prefixes fall anywhere relative to the 128-row
+    query tiles and 64-key tiles; every third case has prefixes long enough
+    for the key range to be split across workgroups."""
+    rng = np.random.default_rng(seed)
+    specs = []
+    for i in range(n):
+        D = int(rng.choice([64, 128]))
+        bs = int(rng.choice([8, 16, 32]))
+        hkv = int(rng.choice([1, 2, 4]))
+        hq = hkv * int(rng.choice([1, 2, 4]))
+        chunk = int(rng.integers(1, 300))
+        prefix = int(rng.integers(1100, 2600)) if i % 3 == 2 else int(rng.integers(0, 400))
+        n_chunks = int(rng.integers(1, 5))
+        specs.append(pf_spec(f"pf_rand{i}_d{D}_bs{bs}_{hq}x{hkv}_c{chunk}_p{prefix}_n{n_chunks}",
+                             hq, hkv, D, bs, chunk, prefix, n_chunks=n_chunks, seed=5000 + i))
+    return specs
+
+
+@pytest.mark.parametrize("spec", _random_prefill_specs(), ids=lambda s: s.name)
+def test_prefill_random_shapes(spec):
+    say("prefill random", spec.name)
+    b = W.make_batch(spec, pad_rows=2)
+    dev = DevBatch(b)
+    dev.append()
+    out = to_host(dev.prefill())
+    kc, vc = check_append(b, dev)
+    check_prefill(b, kc, vc, out)
+
+
 def test_prefill_ragged_chunks():
     say("prefill ragged")
     spec = pf_spec("pf_ragged", 4, 2, 128, 16, 64, 100, n_chunks=4, seed=21)
