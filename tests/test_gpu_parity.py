@@ -195,6 +195,48 @@ def test_decode_edge_lengths(spec, part):
     check_decode(b, kc, vc, out)
 
 
+def _random_decode_cases(n=16, seed=777):
+    """Seeded random shapes over the decode's routing: head dim 64 or 128,
+    block size 1, 8, 16 or 32, 1 to 16 query heads per KV head (vector-ALU
+    and matrix-core kernels, 4, 8 and 16 heads per workgroup), 3 to 40
+    sequences with log-uniform lengths that include 1 and block boundaries,
+    and a partition size of the library's choice, one block, or a random
+    multiple of the block size up to the largest; every other case is
+    dispatched in a random order."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        D = int(rng.choice([64, 128]))
+        bs = int(rng.choice([1, 8, 16, 32]))
+        hkv = int(rng.choice([1, 2, 4]))
+        G = int(rng.choice([1, 2, 3, 4, 6, 8, 12, 16]))
+        n_seqs = int(rng.integers(3, 41))
+        hi = 4096 if bs >= 8 else 1024
+        lens = np.exp(rng.uniform(0.0, np.log(hi), n_seqs)).astype(int).clip(1, hi)
+        lens[0] = 1
+        lens[1] = bs * int(rng.integers(1, 9))  # a full last block
+        spec = gpu_spec(f"dec_rand{i}_d{D}_bs{bs}_{hkv * G}x{hkv}_s{n_seqs}", hkv * G, hkv, D,
+                        bs, tuple(int(L) for L in lens), seed=6000 + i)
+        top = max_partition(spec) // bs
+        part = [0, bs, bs * int(rng.integers(1, top + 1))][i % 3]
+        order = rng.permutation(n_seqs).astype(np.int32) if i % 2 else None
+        cases.append((spec, part, order))
+    return cases
+
+
+@pytest.mark.parametrize("spec,part,order", _random_decode_cases(),
+                         ids=lambda c: c.name if isinstance(c, W.Spec) else None)
+def test_decode_random_shapes(spec, part, order):
+    say("decode random", spec.name, "partition", part,
+        "order", "given" if order is not None else "none")
+    b = W.make_batch(spec, pad_rows=2)
+    dev = DevBatch(b)
+    dev.append()
+    out = to_host(dev.decode(partition_size=part, seq_order=order))
+    kc, vc = check_append(b, dev)
+    check_decode(b, kc, vc, out)
+
+
 def test_decode_long_context():
     # both 4 GiB pools bitwise after the append, every output row
     say("decode long (8 x 32768)")
