@@ -105,6 +105,23 @@ __device__ __forceinline__ void load_lds16(const void *gbase, unsigned off, void
                : "memory", "m0");
 }
 
+// Maxima over the 4 lanes of each column (l, l + 16, l + 32, l + 48) of two
+// values at once: a swap of the halves between the two registers leaves the
+// first value's half-maxima in lanes 0-31 and the second's in lanes 32-63,
+// one swap of 16-lane rows finishes both, and a last swap of the halves
+// gives each register its own maximum in every lane.
+__device__ __forceinline__ void max_over_rows2(float &x, float &y) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y),
+                                                  false, false);
+  const float r = vmax(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const unsigned ru = __float_as_uint(r);
+  const auto b = __builtin_amdgcn_permlane16_swap(ru, ru, false, false);
+  const unsigned s = __float_as_uint(vmax(__uint_as_float(b[0]), __uint_as_float(b[1])));
+  const auto c = __builtin_amdgcn_permlane32_swap(s, s, false, false);
+  x = __uint_as_float(c[0]);
+  y = __uint_as_float(c[1]);
+}
+
 // A tile buffer index known at compile time.
 template <int B>
 struct Buf {
@@ -362,8 +379,11 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p,
 #pragma unroll
         for (int i = 1; i < 15; i += 2)
           tmax = vmax3(tmax, st[i >> 2][qb][i & 3], st[(i + 1) >> 2][qb][(i + 1) & 3]);
-        tm[qb] = max_over_rows(vmax(tmax, st[3][qb][3])) * p.scale_log2e;
+        tm[qb] = vmax(tmax, st[3][qb][3]);
       }
+      max_over_rows2(tm[0], tm[1]);
+      tm[0] *= p.scale_log2e;
+      tm[1] *= p.scale_log2e;
       // Lazy rescaling: the running maximum m only moves when some row's
       // maximum exceeds it by more than 2^8, so weights stay below 256
       // (exact enough in fp16) and the O rescale is rare; one branch serves
