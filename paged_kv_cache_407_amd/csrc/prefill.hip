@@ -82,12 +82,12 @@ __device__ __forceinline__ int vswz(int r) {
 #define PKV_AS1 __attribute__((address_space(1)))
 #define PKV_AS3 __attribute__((address_space(3)))
 
-// 16 bytes from global memory at gbase + off straight into LDS; `gbase` and
-// `lds` must be the same in every lane of the wave (the scalar base address
-// and the instruction's LDS base, in M0), `off` is the lane's byte offset,
-// and lane l writes bytes 16 l .. 16 l + 15 above `lds`.  With the block's
-// base in scalar registers, a tile's loads need no per-lane 64-bit address
-// arithmetic (mixed step 39.5 -> 38.0 us against a full per-lane address).
+// Direct-to-LDS loads of 16 bytes per lane: the global address is a scalar
+// base (the block's, the same in every lane) plus the lane's 32-bit byte
+// offset, and lane l writes bytes 16 l .. 16 l + 15 above the LDS base in
+// M0.  With the block's base in scalar registers, a tile's loads need no
+// per-lane 64-bit address arithmetic (mixed step 39.5 -> 38.0 us against a
+// full per-lane address).
 //
 // Written as the instruction itself rather than the compiler builtin: while
 // the compiler tracks a direct-to-LDS load in flight, it treats the LDS
@@ -97,12 +97,38 @@ __device__ __forceinline__ int vswz(int r) {
 // again.  The instruction writes no register, only LDS; every reader of the
 // buffer it fills runs after this kernel's explicit wait for all memory
 // counters and a barrier.
-__device__ __forceinline__ void load_lds16(const void *gbase, unsigned off, void *lds) {
+//
+// N consecutive 1 KB chunks of one block with one M0: the instruction's
+// immediate offset (k KB for chunk k) is added to both the global address
+// gbase + off[k] and the LDS address lds, so chunk k lands at lds + k KB
+// and reads gbase + off[k] + k KB (one M0 write per block instead of one
+// per load: 0.3-0.9 % faster, bitwise the same).
+template <int N>
+__device__ __forceinline__ void load_lds16_run(const void *gbase, const unsigned *off, void *lds) {
   const unsigned base = (unsigned)(size_t)(PKV_AS3 void *)lds;
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(off), "s"(gbase), "s"(base)
-               : "memory", "m0");
+  if constexpr (N == 1) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(off[0]), "s"(gbase), "s"(base)
+                 : "memory", "m0");
+  } else if constexpr (N == 2) {
+    asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\t"
+                 "global_load_lds_dwordx4 %0, %2\n\t"
+                 "global_load_lds_dwordx4 %1, %2 offset:1024"
+                 :
+                 : "v"(off[0]), "v"(off[1]), "s"(gbase), "s"(base)
+                 : "memory", "m0");
+  } else {
+    static_assert(N == 4, "runs of 1, 2 or 4 chunks");
+    asm volatile("s_mov_b32 m0, %5\n\ts_nop 0\n\t"
+                 "global_load_lds_dwordx4 %0, %4\n\t"
+                 "global_load_lds_dwordx4 %1, %4 offset:1024\n\t"
+                 "global_load_lds_dwordx4 %2, %4 offset:2048\n\t"
+                 "global_load_lds_dwordx4 %3, %4 offset:3072"
+                 :
+                 : "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "s"(gbase), "s"(base)
+                 : "memory", "m0");
+  }
 }
 
 // Maxima over the 4 lanes of each column (l, l + 16, l + 32, l + 48) of two
@@ -215,14 +241,17 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p,
   // the end.  V rows of keys at or past the sequence length (tail slots of
   // the last block, or a clamped block) are zeroed once they have landed:
   // their weights are 0, and 0 times a non-finite value would not be.
+  // Load instructions of one block (JPB) share one M0 and take their
+  // chunk's KB offset from the instruction.
+  constexpr int JPB = (BS / RPI) < NI ? (BS / RPI) : NI;
   unsigned koff[NI], voff[NI];  // byte offsets of the lane's chunks in a block
 #pragma unroll
   for (int j = 0; j < NI; ++j) {
     const int r = 16 * wave + RPI * j + lane / SL;
     const int sl = lane % SL;
     const int kr = r % BS;  // row within its block
-    koff[j] = (kr * D + 8 * (sl ^ kswz<SL>(r))) * 2;
-    voff[j] = (kr * D + 8 * (sl ^ vswz<SL>(r))) * 2;
+    koff[j] = (kr * D + 8 * (sl ^ kswz<SL>(r))) * 2 - 1024 * (j % JPB);
+    voff[j] = (kr * D + 8 * (sl ^ vswz<SL>(r))) * 2 - 1024 * (j % JPB);
   }
   const size_t head_elems = (size_t)BS * D;
   auto tile_ids = [&](int t, int *ids) {
@@ -243,10 +272,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p,
       base[u] = ((size_t)(oob ? 0 : ph) * p.num_kv_heads + kvh) * head_elems;
     }
 #pragma unroll
-    for (int j = 0; j < NI; ++j) {
+    for (int j = 0; j < NI; j += JPB) {
       const int u = (RPI * j) / BS;
-      load_lds16(p.k_cache + base[u], koff[j], kbuf(buf) + (NI * wave + j) * 512);
-      load_lds16(p.v_cache + base[u], voff[j], vbuf(buf) + (NI * wave + j) * 512);
+      load_lds16_run<JPB>(p.k_cache + base[u], &koff[j], kbuf(buf) + (NI * wave + j) * 512);
+      load_lds16_run<JPB>(p.v_cache + base[u], &voff[j], vbuf(buf) + (NI * wave + j) * 512);
     }
   };
   // after this wave's loads of tile t have landed
