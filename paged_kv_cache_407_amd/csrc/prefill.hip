@@ -244,7 +244,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p,
   // Load instructions of one block (JPB) share one M0 and take their
   // chunk's KB offset from the instruction.
   constexpr int JPB = (BS / RPI) < NI ? (BS / RPI) : NI;
-  unsigned koff[NI], voff[NI];  // byte offsets of the lane's chunks in a block
+  // the lane's byte offset in its block, less its load's immediate offset
+  unsigned koff[NI], voff[NI];
 #pragma unroll
   for (int j = 0; j < NI; ++j) {
     const int r = 16 * wave + RPI * j + lane / SL;
