@@ -393,6 +393,9 @@ SMALL_PREFILL = [
     pf_spec("pf_d128_bs16_long", 2, 2, 128, 16, 300, 300, seed=15),
     pf_spec("pf_d128_bs8_gqa", 4, 2, 128, 8, 100, 200, seed=17),
     pf_spec("pf_d64_bs8", 4, 4, 64, 8, 130, 70, seed=18),
+    # 8 and 16 query heads per KV head
+    pf_spec("pf_d128_bs16_gqa8", 16, 2, 128, 16, 90, 250, seed=19),
+    pf_spec("pf_d64_bs32_gqa16", 16, 1, 64, 32, 140, 100, seed=20),
 ]
 
 
